@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for attention forward/backward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never touches it.
+
+Thin ctypes wrapper over ``attn_oracle.c`` (plain C, fp64, OpenMP).  All arrays
+are float64 numpy arrays in BSHD (dense) or packed THD (varlen) layout; LSE and
+delta are (B, H, Sq) or (H, T).  See ``attn_oracle.c`` for the definition each
+function follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+_dp = ctypes.POINTER(ctypes.c_double)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    i, d = ctypes.c_int, ctypes.c_double
+    lib.oracle_attn_fwd.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp]
+    lib.oracle_attn_delta.argtypes = [i, i, i, i, _dp, _dp, _dp]
+    lib.oracle_attn_bwd.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp, _dp, _dp,
+                                    _dp, _dp, _dp]
+    lib.oracle_attn_varlen_fwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp]
+    lib.oracle_attn_varlen_bwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                           _dp, _dp, _dp]
+    for f in ("oracle_attn_fwd", "oracle_attn_delta", "oracle_attn_bwd", "oracle_attn_varlen_fwd",
+              "oracle_attn_varlen_bwd", "oracle_num_threads"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def _m(mask):
+    if mask is None:
+        return None
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    return mask
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError(f"oracle rejected arguments (code {rc})")
+
+
+def attn_fwd(q, k, v, key_mask=None, scale=None):
+    """q (B,Sq,H,D), k/v (B,Sk,H,D) -> out (B,Sq,H,D), lse (B,H,Sq)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    assert k.shape == (B, Sk, H, D) and v.shape == k.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    mask = _m(key_mask)
+    if mask is not None:
+        assert mask.shape == (B, Sk)
+    out = np.empty_like(q)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    _check(_load().oracle_attn_fwd(B, Sq, Sk, H, D, scale, _p(q), _p(k), _p(v),
+                                   None if mask is None else mask.ctypes.data_as(_u8p), _p(out),
+                                   _p(lse)))
+    return out, lse
+
+
+def attn_delta(out, dout):
+    """delta[b,h,i] = <dO[b,i,h,:], out[b,i,h,:]> -> (B,H,S)."""
+    out, dout = _f64(out), _f64(dout)
+    B, S, H, D = out.shape
+    delta = np.empty((B, H, S), dtype=np.float64)
+    _check(_load().oracle_attn_delta(B, S, H, D, _p(out), _p(dout), _p(delta)))
+    return delta
+
+
+def attn_bwd(q, k, v, out, lse, dout, key_mask=None, scale=None, want_dq=True, want_dkdv=True):
+    """Return (delta, dq, dk, dv); dq or dk/dv are None when not requested.
+
+    ``out`` and ``lse`` must come from :func:`attn_fwd` on the same inputs (or,
+    for key-column sampling, from the full forward while k/v are a key subset).
+    """
+    q, k, v, out, lse, dout = map(_f64, (q, k, v, out, lse, dout))
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    mask = _m(key_mask)
+    delta = np.empty((B, H, Sq), dtype=np.float64)
+    dq = np.empty_like(q) if want_dq else None
+    dk = np.empty_like(k) if want_dkdv else None
+    dv = np.empty_like(v) if want_dkdv else None
+    _check(_load().oracle_attn_bwd(B, Sq, Sk, H, D, scale, _p(q), _p(k), _p(v),
+                                   None if mask is None else mask.ctypes.data_as(_u8p), _p(out),
+                                   _p(lse), _p(dout), _p(delta), _p(dq), _p(dk), _p(dv)))
+    return delta, dq, dk, dv
+
+
+def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None):
+    """Packed q/k/v (T,H,D) (a leading batch dim of 1 is accepted) -> out (T,H,D), lse (H,T)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    shp = q.shape
+    T, H, D = shp[-3:]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    assert cu[-1] == T
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty_like(q)
+    lse = np.empty((H, T), dtype=np.float64)
+    _check(_load().oracle_attn_varlen_fwd(len(cu) - 1, cu.ctypes.data_as(_i32p), H, D, scale,
+                                          _p(q), _p(k), _p(v), _p(out), _p(lse)))
+    return out, lse
+
+
+def attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None):
+    """-> (delta (H,T), dq, dk, dv) for packed inputs."""
+    q, k, v, out, lse, dout = map(_f64, (q, k, v, out, lse, dout))
+    T, H, D = q.shape[-3:]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    delta = np.empty((H, T), dtype=np.float64)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    _check(_load().oracle_attn_varlen_bwd(len(cu) - 1, cu.ctypes.data_as(_i32p), H, D, scale,
+                                          _p(q), _p(k), _p(v), _p(out), _p(lse), _p(dout),
+                                          _p(delta), _p(dq), _p(dk), _p(dv)))
+    return delta, dq, dk, dv
