@@ -1,0 +1,211 @@
+// api.hip -- the C ABI of libattn: argument validation on the host, then launches.
+//
+// Every check runs before anything is enqueued, so a call that returns an
+// error has launched nothing and written nothing.  No allocation, no state,
+// no synchronisation: the caller's stream orders the work.
+#include <math.h>
+#include <limits.h>
+
+#include "../../include/libattn.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using attn::BwdParams;
+using attn::FwdParams;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+// A tensor pointer may be NULL only when the tensor has no elements.
+bool missing(const void* ptr, bool has_elements) { return ptr == nullptr && has_elements; }
+
+// Sizes for dense calls; returns ATTN_OK or an error code.
+int check_dense(int B, int Sq, int Sk, int H, int D, float scale) {
+  if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (!scale_ok(scale)) return ATTN_ERR_SHAPE;
+  if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+  // Row indices (b*S + s) and workgroup counts are kept in 32-bit integers.
+  if ((long)B * Sq > INT_MAX || (long)B * Sk > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  if ((cdiv(Sq, 32) + cdiv(Sk, 32)) * H * (long)B > INT_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// Validates the host copy of cu_seqlens; on success sets T and the longest length.
+int check_varlen(int nseq, const int32_t* cu, int H, int D, float scale, int* T, int* maxlen) {
+  if (nseq < 0 || H < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (!scale_ok(scale)) return ATTN_ERR_SHAPE;
+  if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+  if (cu[0] != 0) return ATTN_ERR_SEQLENS;
+  int mx = 0;
+  for (int n = 0; n < nseq; ++n) {
+    if (cu[n + 1] < cu[n]) return ATTN_ERR_SEQLENS;
+    const int len = cu[n + 1] - cu[n];
+    if (len > mx) mx = len;
+  }
+  if (2 * cdiv(mx, 32) * H * (long)nseq > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  *T = cu[nseq];
+  *maxlen = mx;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer argument";
+    case ATTN_ERR_SHAPE: return "invalid size or scale";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim or size";
+    case ATTN_ERR_SEQLENS: return "invalid cu_seqlens";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
+             const void* v, const uint8_t* key_mask, void* out, float* lse, void* stream) {
+  const int st = check_dense(B, Sq, Sk, H, D, scale);
+  if (st != ATTN_OK) return st;
+  const bool has_q = (long)B * Sq * H > 0, has_k = (long)B * Sk * H > 0;
+  if (missing(q, has_q) || missing(out, has_q) || missing(lse, has_q) || missing(k, has_k) ||
+      missing(v, has_k))
+    return ATTN_ERR_NULL;
+  if ((long)B * H * Sq == 0) return ATTN_OK;
+  FwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.mask = key_mask;
+  p.out = static_cast<__bf16*>(out);
+  p.lse = lse;
+  p.cu = nullptr;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.H = H;
+  p.n_qtiles = (int)cdiv(Sq, attn::kFwdBlockM);
+  p.n_blocks = p.n_qtiles * H * B;
+  p.c2 = scale * attn::kLog2e;
+  return status_of(attn::launch_fwd(D, false, p, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_preprocess(int B, int S, int H, int D, const void* out, const void* dout,
+                        float* delta, void* stream) {
+  if (B < 0 || S < 0 || H < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+  const long rows = (long)B * S * H;
+  if (missing(out, rows > 0) || missing(dout, rows > 0) || missing(delta, rows > 0))
+    return ATTN_ERR_NULL;
+  if (rows == 0) return ATTN_OK;
+  if (cdiv(rows, 256 / (D / 8)) > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  return status_of(attn::launch_delta(D, rows, S, H, static_cast<const __bf16*>(out),
+                                      static_cast<const __bf16*>(dout), delta,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+static BwdParams bwd_params(int B, int Sq, int Sk, int H, float scale, const void* q,
+                            const void* k, const void* v, const uint8_t* key_mask,
+                            const float* lse, const float* delta, const void* dout, void* dq,
+                            void* dk, void* dv, const int32_t* cu) {
+  BwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.mask = key_mask;
+  p.lse = lse;
+  p.delta = delta;
+  p.dout = static_cast<const __bf16*>(dout);
+  p.dq = static_cast<__bf16*>(dq);
+  p.dk = static_cast<__bf16*>(dk);
+  p.dv = static_cast<__bf16*>(dv);
+  p.cu = cu;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.H = H;
+  p.c2 = scale * attn::kLog2e;
+  p.scale = scale;
+  return p;
+}
+
+int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
+             const void* v, const uint8_t* key_mask, const float* lse, const float* delta,
+             const void* dout, void* dq, void* dk, void* dv, void* stream) {
+  const int st = check_dense(B, Sq, Sk, H, D, scale);
+  if (st != ATTN_OK) return st;
+  const bool hq = (long)B * Sq * H > 0, hk = (long)B * Sk * H > 0;
+  if (missing(q, hq) || missing(lse, hq) || missing(delta, hq) || missing(dout, hq) ||
+      missing(dq, hq) || missing(k, hk) || missing(v, hk) || missing(dk, hk) || missing(dv, hk))
+    return ATTN_ERR_NULL;
+  if ((long)B * H == 0) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BwdParams p = bwd_params(B, Sq, Sk, H, scale, q, k, v, key_mask, lse, delta, dout, dq, dk, dv,
+                           nullptr);
+  p.n_kv_tiles = (int)cdiv(Sk, attn::kDkvBlockN);
+  p.n_q_tiles = (int)cdiv(Sq, attn::kDqBlockM);
+  p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * B;
+  return status_of(attn::launch_bwd(D, false, p, s));
+}
+
+int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                    int H, int D, float scale, const void* q, const void* k, const void* v,
+                    void* out, float* lse, void* stream) {
+  if (!cu_seqlens_host || !cu_seqlens_dev) return ATTN_ERR_NULL;
+  int T = 0, maxlen = 0;
+  const int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
+  if (st != ATTN_OK) return st;
+  const bool ht = (long)T * H > 0;
+  if (missing(q, ht) || missing(k, ht) || missing(v, ht) || missing(out, ht) || missing(lse, ht))
+    return ATTN_ERR_NULL;
+  if ((long)T * H == 0) return ATTN_OK;
+  FwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.mask = nullptr;
+  p.out = static_cast<__bf16*>(out);
+  p.lse = lse;
+  p.cu = cu_seqlens_dev;
+  p.B = nseq;
+  p.Sq = p.Sk = T;
+  p.H = H;
+  p.n_qtiles = (int)cdiv(maxlen, attn::kFwdBlockM);
+  p.n_blocks = p.n_qtiles * H * nseq;
+  p.c2 = scale * attn::kLog2e;
+  return status_of(attn::launch_fwd(D, true, p, static_cast<hipStream_t>(stream)));
+}
+
+int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                    int H, int D, float scale, const void* q, const void* k, const void* v,
+                    const float* lse, const float* delta, const void* dout, void* dq, void* dk,
+                    void* dv, void* stream) {
+  if (!cu_seqlens_host || !cu_seqlens_dev) return ATTN_ERR_NULL;
+  int T = 0, maxlen = 0;
+  const int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
+  if (st != ATTN_OK) return st;
+  const bool ht = (long)T * H > 0;
+  if (missing(q, ht) || missing(k, ht) || missing(v, ht) || missing(lse, ht) ||
+      missing(delta, ht) || missing(dout, ht) || missing(dq, ht) || missing(dk, ht) ||
+      missing(dv, ht))
+    return ATTN_ERR_NULL;
+  if ((long)T * H == 0) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BwdParams p = bwd_params(nseq, T, T, H, scale, q, k, v, nullptr, lse, delta, dout, dq, dk, dv,
+                           cu_seqlens_dev);
+  p.n_kv_tiles = (int)cdiv(maxlen, attn::kDkvBlockN);
+  p.n_q_tiles = (int)cdiv(maxlen, attn::kDqBlockM);
+  p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * nseq;
+  return status_of(attn::launch_bwd(D, true, p, s));
+}
+
+}  // extern "C"

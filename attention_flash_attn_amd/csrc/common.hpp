@@ -1,0 +1,86 @@
+// common.hpp -- device helpers shared by the libattn kernels (gfx950 only).
+//
+// MFMA operand layouts used throughout (wave64, v_mfma_f32_32x32x16_bf16):
+//   A (32 x 16):  lane l holds row l%32, reduction slots 8*(l/32) .. +7
+//   B (16 x 32):  lane l holds column l%32, reduction slots 8*(l/32) .. +7
+//   C (32 x 32):  lane l holds column l%32; register r holds row
+//                 8*(r/4) + 4*(l/32) + r%4
+// Any fixed assignment of reduction slots to a real index works as long as A
+// and B agree, which is how score tiles are fed back in as operands without a
+// shuffle (see kRowPerm).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row permutation inside a 32-row block: swaps bit 2 and bit 3 of the index.
+// If LDS row p of a tile holds tile row kRowPerm(p), then a 32x32 MFMA result
+// whose rows come from LDS rows 0..31 has, in lane half h, registers
+// r = 8t + s (t in {0,1}, s in 0..7) holding tile row 16t + 8h + s: eight
+// consecutive rows per register octet, exactly the B-operand slot order of the
+// next MFMA step.  The permutation is an involution.
+__device__ __forceinline__ int kRowPerm(int p) {
+  return (p & 0x13) | ((p & 0x8) >> 1) | ((p & 0x4) << 1);
+}
+
+// Register r of a 32x32 C tile in lane half h holds (after kRowPerm) tile row:
+__device__ __forceinline__ int c_row_permuted(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+// 16-byte global load / store as raw bits.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// LDS transposing read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// destination lane j, element e receives element (j%4) of the 4-element chunk
+// addressed by source lane 4*e + j/4 of the same group.
+__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Eight fp32 values -> bf16x8 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)v[base + i];
+  return r;
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs; renumber them so that each
+// XCD receives one contiguous range of logical tiles (neighbouring tiles share
+// K/V and stay in that XCD's L2).  Bijective for any n.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+__device__ __forceinline__ float wave_max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
+}  // namespace attn

@@ -1,0 +1,53 @@
+// kernels.hpp -- launch parameters shared between the host entry points and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Dense problems: outer index = batch, rows of batch b start at b*Sq (q) / b*Sk (k).
+// Varlen problems: outer index = sequence n, rows [cu[n], cu[n+1]); Sq = Sk = T.
+struct FwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const uint8_t* mask;  // dense only: (B, Sk) bytes or null
+  __bf16* out;
+  float* lse;
+  const int32_t* cu;  // varlen only (device)
+  int B, Sq, Sk, H;
+  int n_qtiles;  // query tiles per (outer, head)
+  int n_blocks;
+  float c2;  // scale * log2(e)
+};
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const uint8_t* mask;
+  const float* lse;
+  const float* delta;
+  const __bf16* dout;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  const int32_t* cu;
+  int B, Sq, Sk, H;
+  int n_kv_tiles;  // dK/dV workgroups per (outer, head)
+  int n_q_tiles;   // dQ workgroups per (outer, head)
+  int n_blocks;
+  float c2;     // scale * log2(e)
+  float scale;
+};
+
+constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
+constexpr int kDqBlockM = 128;    // query rows per dQ workgroup
+constexpr int kDkvBlockN = 128;   // key rows per dK/dV workgroup
+
+hipError_t launch_fwd(int D, bool varlen, const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(int D, bool varlen, const BwdParams& p, hipStream_t stream);
+hipError_t launch_delta(int D, long rows, int S, int H, const __bf16* out, const __bf16* dout,
+                        float* delta, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,165 @@
+"""Benchmark: attention fwd+bwd on one MI355X, BSHD bf16, non-causal.
+
+A step is one pass of the whole path on one batch of resident synthetic input:
+    attn_fwd -> attn_bwd_preprocess -> attn_bwd
+on the per-rank shard of the Wan attention layer that LightX2V PR #1234 times
+("Performance": N=27280, 40 heads over 4 sequence-parallel ranks -> 10 heads,
+D=128, bf16): B=1, S=27280, H=10, D=128, q/k/v/dO ~ N(0,1) rounded to bf16.
+
+Throughput is algorithmic attention FLOPs (forward 4*B*H*S^2*D, backward 2.5x
+that) over the measured step time.  Each library call is one kernel, and
+hipEvents recorded around each call on the launch stream give every kernel's
+average duration inside the timed region; the dominant kernel's roofline line
+uses its own algorithmic FLOPs and that duration.  The fp64 CPU oracle is
+timed beside it on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, Wan shard N=27280 H=10 D=128"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan_shard")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=27280,
+                    help="query rows of one head in the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, t, rows):
+    """fp64 oracle on one head, the first `rows` query rows against all keys: forward,
+    delta, dQ of those rows and their full dK/dV contribution (same per-row work as
+    the full problem)."""
+    import numpy as np
+
+    import oracle
+    from attention_flash_attn_amd import inputs as I
+
+    h = 0
+    q, k, v, do = (I.f64_from_bf16_bits(x[:1, :, h:h + 1]) for x in (t.q, t.k, t.v, t.do))
+    q, do = q[:, :rows], do[:, :rows]
+    t0 = time.perf_counter()
+    out, lse = oracle.attn_fwd(q, k, v)
+    oracle.attn_bwd(q, k, v, out, lse, do)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * 4.0 * rows * k.shape[1] * w.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"one head (b=0,h=0), {rows} of {w.S} query rows x all {k.shape[1]} keys, "
+                      f"fwd+delta+dQ+dK/dV in fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the attention path here has no multi-GPU "
+              "mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_flash_attn_amd as A
+    from attention_flash_attn_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    A.lib()
+    w = I.WORKLOADS[args.workload]
+    assert not w.varlen and w.valid_lens is None, "bench times the dense unmasked workload"
+    t = I.draw_workload(w)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = (dev(x) for x in (t.q, t.k, t.v, t.do))
+    B, S, H, D = w.B, w.S, w.H, w.D
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        A.attn_fwd(q, k, v, None, None, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        A.attn_bwd_preprocess(out, do, delta=delta)
+        if ev is not None:
+            ev[2].record()
+        A.attn_bwd(q, k, v, lse, delta, do, None, None, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                    for e in evs])  # ms
+    step_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / K
+    fwd_ms, pre_ms, bwd_ms = (float(x) for x in per.mean(0))
+
+    f_fwd = w.fwd_flops()
+    f_bwd = 2.5 * f_fwd
+    total = f_fwd + f_bwd
+    value = total / (step_ms / 1e3) / 1e12
+    kernels = {"attn_fwd": (fwd_ms, f_fwd), "attn_bwd": (bwd_ms, f_bwd)}
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dom_ms, dom_flops = kernels[dom]
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: q,k,v,dO ~ N(0,1) seed 4, rounded to bf16",
+        "config": {"workload": f"{w.name}: B={B} N={S} H={H} D={D}, BSHD bf16, non-causal, "
+                               "no mask (one Ulysses rank of the 40-head Wan layer)",
+                   "batch": B, "seq_len": S, "heads": H, "head_dim": D, "parallelism": "none"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"attn_fwd": round(fwd_ms, 4), "attn_bwd_preprocess": round(pre_ms, 4),
+                       "attn_bwd": round(bwd_ms, 4)},
+        "fwd_tflops": round(f_fwd / (fwd_ms / 1e3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (bwd_ms / 1e3) / 1e12, 2),
+        "wall_ms_per_step": round(1e3 * wall / K, 4),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

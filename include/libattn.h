@@ -1,0 +1,121 @@
+/*
+ * libattn.h -- scaled-dot-product attention forward/backward for AMD MI355X (gfx950).
+ *
+ * The operation is the per-GPU attention a Ulysses sequence-parallel rank runs
+ * once the all-to-all has handed it the full sequence and its share of the
+ * heads (LightX2V PR #1234, "Performance": the Ulysses attention layer;
+ * diffusers PR #14834, summary).  It is non-causal, dropout-free attention
+ * (diffusers PR #14341, "Not verified") over BSHD tensors: the forward op
+ * returns out in BSHD and the backward op consumes grad_out in BSHD, with K/V
+ * read in the very layout they were handed in (diffusers PR #14341, body: the
+ * K/V double-transpose fix).  For one (batch, head), query row i, key row j:
+ *
+ *   s_ij = scale * <q_i, k_j>, masked keys excluded (a bool key mask acts as a
+ *          0 / -inf additive bias: diffusers PR #14341, follow-up 2)
+ *   LSE_i = log sum_j exp(s_ij)        natural log, fp32, always produced
+ *   out_i = sum_j exp(s_ij - LSE_i) v_j
+ *   delta_i = <dO_i, out_i>
+ *   dS_ij = P_ij (<dO_i, v_j> - delta_i),  P_ij = exp(s_ij - LSE_i)
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
+ *
+ * LSE is an auxiliary output with no gradient (diffusers PR #14834, summary),
+ * and the backward needs it: a forward that skipped it broke training
+ * (diffusers PR #14341, follow-up 1), so every forward here writes it.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are bf16 (raw 16-bit patterns), contiguous.  Dense BSHD element
+ *    (b,s,h,d) is at ((b*S + s)*H + h)*D + d.  Varlen tensors are packed
+ *    (T, H, D), i.e. BSHD with B = 1 and S = T.
+ *  - lse and delta are fp32, (B, H, Sq) row-major; varlen: (H, T).
+ *  - key_mask: NULL (attend to every key) or (B, Sk) bytes, nonzero = attend.
+ *    It is broadcast over heads and queries, i.e. a (B,1,1,Sk) mask.  A
+ *    per-head (B,H,1,Sk) mask is not expressible and must be rejected by the
+ *    caller before any work (diffusers PR #14834, "Unsupported cases").
+ *  - Supported: head dim D in {64, 128}; Hk == H (no GQA); Sq may differ from Sk.
+ *  - A query row whose keys are all masked gets out = 0, LSE = -inf, dQ = 0.
+ *  - A tensor pointer may be NULL only when that tensor has no elements (e.g. k
+ *    and v when Sk = 0); otherwise NULL is ATTN_ERR_NULL.
+ *  - Every tensor pointer is device memory the caller allocated and owns; the
+ *    library allocates nothing, keeps no state and is reentrant.  Calls only
+ *    enqueue work on `stream` (a hipStream_t; NULL = the default stream) and
+ *    never synchronise.  Inputs must not alias outputs.
+ *  - Every argument is checked on the host before any launch.  A call that
+ *    returns an error has enqueued nothing and written nothing.  Nothing aborts.
+ *  - Zero-sized problems (B, H, Sq or T = 0) return ATTN_OK and launch nothing.
+ */
+#ifndef LIBATTN_H
+#define LIBATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is negative, or scale is not finite and > 0 */
+  ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, or a size beyond the index range */
+  ATTN_ERR_SEQLENS = 4,     /* cu_seqlens is not 0 = c0 <= c1 <= ... <= c_nseq = T */
+  ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
+} attn_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_str(int status);
+
+/* ABI revision of this header; bumped on any signature change. */
+int attn_abi_version(void);
+
+/*
+ * Forward: q (B,Sq,H,D), k and v (B,Sk,H,D) bf16 -> out (B,Sq,H,D) bf16 and
+ * lse (B,H,Sq) fp32.  scale multiplies q.k (callers normally pass 1/sqrt(D)).
+ * key_mask may be NULL.
+ */
+int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
+             const void* v, const uint8_t* key_mask, void* out, float* lse, void* stream);
+
+/*
+ * Backward preprocess: delta[b,h,i] = sum_d dO[b,i,h,d] * out[b,i,h,d] in fp32,
+ * from the bf16 out the forward wrote.  out, dout (B,S,H,D) -> delta (B,H,S).
+ * For varlen data call it with B = 1, S = T (delta is a per-row quantity).
+ */
+int attn_bwd_preprocess(int B, int S, int H, int D, const void* out, const void* dout,
+                        float* delta, void* stream);
+
+/*
+ * Backward: from q, k, v, the forward's lse, the preprocess's delta and dout,
+ * write dq (B,Sq,H,D), dk and dv (B,Sk,H,D), all bf16.  Keys excluded by
+ * key_mask get dk = dv = 0 exactly.  dK/dV and dQ are produced by separate
+ * workgroups (of one launch), each owning its output rows, so no atomics are
+ * used and results are bitwise reproducible.  key_mask may be NULL.
+ */
+int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
+             const void* v, const uint8_t* key_mask, const float* lse, const float* delta,
+             const void* dout, void* dq, void* dk, void* dv, void* stream);
+
+/*
+ * Packed variable-length forward (the FA3-varlen path of diffusers PR #14834,
+ * "Model test coverage"): nseq sequences packed back to back in q, k, v
+ * (T, H, D); sequence n owns rows [cu[n], cu[n+1]) and attends only to its own
+ * keys (block-diagonal, non-causal).  cu_seqlens_host and cu_seqlens_dev are
+ * the same int32[nseq+1] array in host and device memory: the host copy is
+ * validated (cu[0] = 0, non-decreasing) and sizes the launch; the kernels read
+ * the device copy.  T = cu[nseq].  lse is (H, T).  No key mask in varlen mode.
+ */
+int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                    int H, int D, float scale, const void* q, const void* k, const void* v,
+                    void* out, float* lse, void* stream);
+
+/* Packed variable-length backward; arguments as in attn_varlen_fwd and attn_bwd.
+ * delta comes from attn_bwd_preprocess(1, T, H, D, out, dout, delta). */
+int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                    int H, int D, float scale, const void* q, const void* k, const void* v,
+                    const float* lse, const float* delta, const void* dout, void* dq, void* dk,
+                    void* dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_H */

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+entry point include/libattn.h declares, and rejects bad arguments with the documented
+status code before touching the device (so these calls never launch anything)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_flash_attn_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libattn.h")
+
+OK, NULL, SHAPE, UNSUP, SEQ = 0, 1, 2, 3, 4
+# A non-null address that is never dereferenced: every call below fails validation
+# (or is zero-sized) before any device work.
+P = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(A.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    return A.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert {"attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_varlen_fwd",
+            "attn_varlen_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.attn_abi_version() == 1
+    assert L.attn_status_str(0) == b"ok"
+    assert L.attn_status_str(4) == b"invalid cu_seqlens"
+
+
+def test_status_enum_matches_header():
+    text = open(HEADER).read()
+    enum = dict((k, int(v)) for k, v in re.findall(r"(ATTN_\w+)\s*=\s*(\d+)", text))
+    assert {v: k for k, v in enum.items()} == A.STATUS
+
+
+def fwd(L, B=1, Sq=8, Sk=8, H=2, D=64, scale=0.125, q=P, k=P, v=P, m=None, out=P, lse=P):
+    return L.attn_fwd(B, Sq, Sk, H, D, scale, q, k, v, m, out, lse, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, q=None) == NULL
+    assert fwd(L, lse=None) == NULL
+    assert fwd(L, B=-1) == SHAPE
+    assert fwd(L, Sk=-3) == SHAPE
+    assert fwd(L, scale=0.0) == SHAPE
+    assert fwd(L, scale=float("nan")) == SHAPE
+    assert fwd(L, scale=float("inf")) == SHAPE
+    for D in (0, 32, 96, 256):
+        assert fwd(L, D=D) == UNSUP
+    assert fwd(L, B=2, Sq=2 ** 30 + 1) == UNSUP
+    # zero-sized problems succeed without launching anything
+    assert fwd(L, B=0) == OK
+    assert fwd(L, Sq=0) == OK
+    assert fwd(L, H=0) == OK
+
+
+def test_preprocess_and_bwd_validation(L):
+    assert L.attn_bwd_preprocess(1, 8, 2, 64, P, None, P, None) == NULL
+    assert L.attn_bwd_preprocess(1, -8, 2, 64, P, P, P, None) == SHAPE
+    assert L.attn_bwd_preprocess(1, 8, 2, 80, P, P, P, None) == UNSUP
+    assert L.attn_bwd_preprocess(0, 8, 2, 64, P, P, P, None) == OK
+    args = [1, 8, 8, 2, 64, 0.125, P, P, P, None, P, P, P, P, P, P, None]
+    for i in (6, 7, 8, 10, 11, 12, 13, 14, 15):  # every tensor but the mask is required
+        a = list(args)
+        a[i] = None
+        assert L.attn_bwd(*a) == NULL, i
+    a = list(args)
+    a[4] = 48
+    assert L.attn_bwd(*a) == UNSUP
+    a = list(args)
+    a[5] = -1.0
+    assert L.attn_bwd(*a) == SHAPE
+    a = list(args)
+    a[0] = 0
+    assert L.attn_bwd(*a) == OK
+
+
+def _cu(vals):
+    arr = np.array(vals, dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_varlen_validation(L):
+    def call(vals, nseq=None, H=2, D=128):
+        arr, p = _cu(vals)
+        n = len(vals) - 1 if nseq is None else nseq
+        f = L.attn_varlen_fwd(n, p, P, H, D, 0.1, P, P, P, P, P, None)
+        b = L.attn_varlen_bwd(n, p, P, H, D, 0.1, P, P, P, P, P, P, P, P, P, None)
+        return f, b
+
+    assert call([1, 5, 9]) == (SEQ, SEQ)        # must start at 0
+    assert call([0, 5, 4]) == (SEQ, SEQ)        # must not decrease
+    assert call([0, 5, 9], D=72) == (UNSUP, UNSUP)
+    assert call([0, 5, 9], nseq=-1) == (SHAPE, SHAPE)
+    assert call([0]) == (OK, OK)                # no sequences: nothing to do
+    assert call([0, 0, 0]) == (OK, OK)          # empty sequences: T = 0
+    assert call([0, 5, 9], H=0) == (OK, OK)
+    arr, p = _cu([0, 4])
+    assert L.attn_varlen_fwd(1, None, P, 2, 64, 0.1, P, P, P, P, P, None) == NULL
+    assert L.attn_varlen_fwd(1, p, None, 2, 64, 0.1, P, P, P, P, P, None) == NULL
+
+
+def test_binding_rejects_per_head_mask_and_bad_shapes():
+    torch = pytest.importorskip("torch")
+    # Shape checks run before any device use; a CPU meta tensor is enough to reach them.
+    B, S, H, D = 2, 16, 4, 64
+    m = torch.ones((B, H, 1, S), dtype=torch.bool)
+    with pytest.raises(ValueError, match="head-broadcast"):
+        A._mask_arg(m, B, S, H)
+    with pytest.raises(ValueError):
+        A._mask_arg(torch.ones((B, S + 1), dtype=torch.bool), B, S, H)
+    q = torch.empty((B, S, H, D), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        A._want(q, "q", (B, S, H, D), torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        A._want(q, "k", (B, H, S, D), torch.bfloat16)  # a K/V handed over in BHSD
+    with pytest.raises(TypeError):
+        A._want(q.float(), "q", (B, S, H, D), torch.bfloat16)
