@@ -17,9 +17,10 @@
 // dK/dV kernel: one workgroup = 4 waves = 128 keys; each wave keeps its 32
 // keys' K and V rows in registers (B operands of S = Q K^T and dP = dO V^T,
 // so the score tile has one key per lane) and its dK^T, dV^T accumulators in
-// registers across the whole loop over query tiles.  Query tiles (Q, dO rows,
-// LSE, delta) are double-buffered through LDS; Q^T and dO^T operands come from
-// the LDS transposing read.
+// registers across the whole loop over query tiles.  Query tiles of 64 rows
+// (Q, dO, LSE, delta) are double-buffered in LDS, filled asynchronously by
+// global_load_lds into XOR-swizzled rows (tile.hpp); Q^T and dO^T operands come
+// from the LDS transposing read.
 //
 // Both run in ONE launch: the grid is grouped per (batch|sequence, head), each group
 // holding that head's dK/dV workgroups followed by its dQ workgroups, and groups
@@ -30,10 +31,14 @@
 // dQ kernel: one workgroup = 4 waves = 128 query rows; each wave keeps Q and
 // dO rows (B operands of S^T = K Q^T and dP^T = V dO^T: one query per lane, so
 // LSE and delta are per-lane scalars) and its dQ^T accumulator in registers;
-// K/V tiles of 64 keys are double-buffered through LDS; K^T comes from the
-// transposing read.
+// K/V tiles of 64 keys are double-buffered in LDS the same way; K^T comes from
+// the transposing read.
+//
+// Partial tiles (a ragged tail, a mask edge) take separate code paths, so full
+// tiles carry no per-element mask work.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile.hpp"
 
 namespace attn {
 
@@ -114,31 +119,39 @@ __device__ __forceinline__ float pick16(const f32x4& a, const f32x4& b, const f3
 
 template <int D>
 struct DkdvSmem {
-  static constexpr int BQ = 32, QS = D + 8;
-  bf16 q[2][BQ * QS];
-  bf16 o[2][BQ * QS];
+  static constexpr int BQ = 64;  // query rows per staged tile (two 32-row sub-tiles)
+  char q[2][BQ * 2 * D];
+  char o[2][BQ * 2 * D];
   float l[2][BQ];
   float d[2][BQ];
 };
 
 template <int D>
 struct DqSmem {
-  static constexpr int BN = 64, KS = D + 8;
-  bf16 k[2][BN * KS];
-  bf16 v[2][BN * KS];
+  static constexpr int BN = 64;  // keys per staged tile
+  char k[2][BN * 2 * D];
+  char v[2][BN * 2 * D];
 };
+
+// Per-lane offsets of the transposing reads of a kRowPerm-ordered 32-row block: for
+// lane group g and source lane src, reduction half `half` of MFMA step t covers tile
+// rows 16t + 8*(g/2) + 4*half + src/4, stored at LDS row 16t + 8*half + 4*(g/2) + src/4.
+template <int D>
+__device__ __forceinline__ void perm_tr_offsets(int lane, int (&off)[D / 32][2]) {
+  const int g = lane >> 4, src = lane & 15;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      off[mb][half] = tile_off_tr<D>(8 * half + 4 * (g >> 1) + (src >> 2),
+                                     32 * mb + 16 * (g & 1) + 4 * (src & 3));
+}
 
 template <int D, bool VARLEN>
 __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, DkdvSmem<D>& sm) {
   constexpr int BN = 128, BQ = DkdvSmem<D>::BQ;
-  constexpr int QS = DkdvSmem<D>::QS;
+  constexpr int RB = 2 * D;
   constexpr int NKS = D / 16, NMB = D / 32;
-  constexpr int CPR = D / 8, RPP = 256 / CPR;
-  constexpr int NPASS = (BQ + RPP - 1) / RPP;
-  auto& sQ = sm.q;
-  auto& sO = sm.o;
-  auto& sL = sm.l;
-  auto& sDl = sm.d;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -150,120 +163,109 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   const int key = kb0 + wave * 32 + l32;
   bool kvalid = key < nk;
   if (kvalid && sl.mask) kvalid = sl.mask[key] != 0;
-  const bool wave_live = __ballot(kvalid) != 0;
+  const uint64_t kball = __ballot(kvalid);
 
+  // This lane's key row: B operand of S = Q K^T and dP = dO V^T.
   bf16x8 kreg[NKS], vreg[NKS];
   {
-    const long off = ((long)sl.krow0 + key) * rs + (long)sl.head * D + 8 * hl;
+    const long off = ((long)sl.krow0 + min(key, nk - 1)) * rs + (long)sl.head * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const u32x4 z = {0, 0, 0, 0};
-      kreg[ks] = as_bf16x8(key < nk ? ld16(p.k + off + 16 * ks) : z);
-      vreg[ks] = as_bf16x8(key < nk ? ld16(p.v + off + 16 * ks) : z);
+      kreg[ks] = as_bf16x8(ld16(p.k + off + 16 * ks));
+      vreg[ks] = as_bf16x8(ld16(p.v + off + 16 * ks));
     }
   }
 
+  int qoff[NKS], troff[NMB][2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qoff[ks] = tile_off<D>(l32, 2 * ks + hl);
+  perm_tr_offsets<D>(lane, troff);
+
   const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.head * D;
   const bf16* obase = p.dout + (long)sl.qrow0 * rs + (long)sl.head * D;
-  const int sc = tid % CPR, sr0 = tid / CPR;
-  u32x4 qr[NPASS], dr[NPASS];
   float lr = 0.f, dl = 0.f;
-  auto load_tile = [&](int q0) {
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = sr0 + i * RPP;
-      const int qi = q0 + r;
-      const u32x4 z = {0, 0, 0, 0};
-      const bool ok = r < BQ && qi < nq;
-      qr[i] = ok ? ld16(qbase + (long)qi * rs + 8 * sc) : z;
-      dr[i] = ok ? ld16(obase + (long)qi * rs + 8 * sc) : z;
-    }
+  auto issue = [&](int q0, int buf) {
+    const int last = nq - 1;
+    auto row = [&](int r) { return min(q0 + ((r & ~31) | kRowPerm(r & 31)), last); };
+    tile_load_async<D, BQ, 4>(sm.q[buf], qbase, rs, row);
+    tile_load_async<D, BQ, 4>(sm.o[buf], obase, rs, row);
     if (tid < BQ) {
       const int qi = q0 + tid;
       lr = qi < nq ? p.lse[sl.lse_base + qi] * kLog2e : INFINITY;
       dl = qi < nq ? p.delta[sl.lse_base + qi] : 0.f;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = sr0 + i * RPP;
-      if (r < BQ) {
-        const int rq = (r & ~31) | kRowPerm(r & 31);
-        *reinterpret_cast<u32x4*>(&sQ[buf][rq * QS + 8 * sc]) = qr[i];
-        *reinterpret_cast<u32x4*>(&sO[buf][rq * QS + 8 * sc]) = dr[i];
-      }
-    }
+  auto publish_stats = [&](int buf) {
     if (tid < BQ) {
-      sL[buf][tid] = lr;
-      sDl[buf][tid] = dl;
+      sm.l[buf][tid] = lr;
+      sm.d[buf][tid] = dl;
     }
   };
-
-  const int g = lane >> 4, src = lane & 15;
-  const int tr_off = (4 * (g >> 1) + (src >> 2)) * QS + 16 * (g & 1) + 4 * (src & 3);
 
   f32x16 dkacc[NMB], dvacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
   const float c2 = p.c2;
 
-  const int ntiles = (nq + BQ - 1) / BQ;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ntiles;
-    if (more) load_tile((j + 1) * BQ);
-    if (wave_live) {
-      const bf16* sQb = sQ[buf];
-      const bf16* sOb = sO[buf];
+  auto compute = [&](auto masked, int buf) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const char* qt = sm.q[buf];
+    const char* ot = sm.o[buf];
+#pragma unroll
+    for (int sub = 0; sub < BQ / 32; ++sub) {
+      const int rb = sub * 32 * RB;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQb[l32 * QS + 16 * ks + 8 * hl]);
-        s = mfma32(a, kreg[ks], s);
-      }
+      for (int ks = 0; ks < NKS; ++ks) s = mfma32(lds_row16(qt, rb + qoff[ks]), kreg[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sOb[l32 * QS + 16 * ks + 8 * hl]);
-        dp = mfma32(a, vreg[ks], dp);
-      }
-      // Register r holds query 16*(r/8) + 8*hl + r%8 of the tile.
-      const float* Lp = &sL[buf][8 * hl];
-      const float* Dp = &sDl[buf][8 * hl];
+      for (int ks = 0; ks < NKS; ++ks) dp = mfma32(lds_row16(ot, rb + qoff[ks]), vreg[ks], dp);
+      // Register r holds query 32*sub + 16*(r/8) + 8*hl + r%8 of the tile.
+      const float* Lp = &sm.l[buf][32 * sub + 8 * hl];
+      const float* Dp = &sm.d[buf][32 * sub + 8 * hl];
       const f32x4 L0 = *reinterpret_cast<const f32x4*>(Lp), L1 = *reinterpret_cast<const f32x4*>(Lp + 4);
       const f32x4 L2 = *reinterpret_cast<const f32x4*>(Lp + 16), L3 = *reinterpret_cast<const f32x4*>(Lp + 20);
       const f32x4 D0 = *reinterpret_cast<const f32x4*>(Dp), D1 = *reinterpret_cast<const f32x4*>(Dp + 4);
       const f32x4 D2 = *reinterpret_cast<const f32x4*>(Dp + 16), D3 = *reinterpret_cast<const f32x4*>(Dp + 20);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = kvalid ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r))) : 0.f;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r)));
+        if (MASKED) pr = kvalid ? pr : 0.f;
         s[r] = pr;
         dp[r] = pr * (dp[r] - pick16(D0, D1, D2, D3, r));
       }
-      bf16x8 pk[2], dsk[2];
-      pk[0] = pack8(s, 0);
-      pk[1] = pack8(s, 8);
-      dsk[0] = pack8(dp, 0);
-      dsk[1] = pack8(dp, 8);
+      const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
+      const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16* op = sOb + 16 * t * QS + 32 * mb + tr_off;
-          const bf16x8 ao = cat_tr(lds_read_tr16(op), lds_read_tr16(op + 8 * QS));
-          dvacc[mb] = mfma32(ao, pk[t], dvacc[mb]);
-          const bf16* qp = sQb + 16 * t * QS + 32 * mb + tr_off;
-          const bf16x8 aq = cat_tr(lds_read_tr16(qp), lds_read_tr16(qp + 8 * QS));
-          dkacc[mb] = mfma32(aq, dsk[t], dkacc[mb]);
-        }
+      for (int mb = 0; mb < NMB; ++mb) {
+        dvacc[mb] = mfma32(lds_tr8(ot + rb, troff[mb][0], troff[mb][1]), pk0, dvacc[mb]);
+        dvacc[mb] = mfma32(lds_tr8(ot + rb + 16 * RB, troff[mb][0], troff[mb][1]), pk1, dvacc[mb]);
+        dkacc[mb] = mfma32(lds_tr8(qt + rb, troff[mb][0], troff[mb][1]), ds0, dkacc[mb]);
+        dkacc[mb] = mfma32(lds_tr8(qt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds1, dkacc[mb]);
+      }
     }
-    if (more) store_tile(buf ^ 1);
+  };
+
+  const int ntiles = (nq + BQ - 1) / BQ;
+  auto step = [&](int j, int buf) {
+    const bool more = j + 1 < ntiles;
+    if (more) issue((j + 1) * BQ, buf ^ 1);
+    if (kball == ~0ull)
+      compute(Flag<false>{}, buf);
+    else if (kball != 0)
+      compute(Flag<true>{}, buf);
+    if (more) publish_stats(buf ^ 1);
+    wait_tile_loads();
     __syncthreads();
+  };
+  if (ntiles > 0) {
+    issue(0, 0);
+    publish_stats(0);
+    wait_tile_loads();
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < ntiles) step(j + 1, 1);
   }
 
   if (key < nk) {
@@ -289,11 +291,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 template <int D, bool VARLEN>
 __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqSmem<D>& sm) {
   constexpr int BM = 128, BN = DqSmem<D>::BN;
-  constexpr int KS = DqSmem<D>::KS;
+  constexpr int RB = 2 * D;
   constexpr int NKS = D / 16, NMB = D / 32;
-  constexpr int CPR = D / 8, RPP = 256 / CPR, NPASS = BN / RPP;
-  auto& sK = sm.k;
-  auto& sV = sm.v;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -305,38 +304,28 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const int qrow = qb + wave * 32 + l32;
   bf16x8 qreg[NKS], doreg[NKS];
   {
-    const long off = ((long)sl.qrow0 + qrow) * rs + (long)sl.head * D + 8 * hl;
+    const long off = ((long)sl.qrow0 + min(qrow, nq - 1)) * rs + (long)sl.head * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const u32x4 z = {0, 0, 0, 0};
-      qreg[ks] = as_bf16x8(qrow < nq ? ld16(p.q + off + 16 * ks) : z);
-      doreg[ks] = as_bf16x8(qrow < nq ? ld16(p.dout + off + 16 * ks) : z);
+      qreg[ks] = as_bf16x8(ld16(p.q + off + 16 * ks));
+      doreg[ks] = as_bf16x8(ld16(p.dout + off + 16 * ks));
     }
   }
   const float lse2 = qrow < nq ? p.lse[sl.lse_base + qrow] * kLog2e : INFINITY;
   const float dl = qrow < nq ? p.delta[sl.lse_base + qrow] : 0.f;
 
+  int koff[NKS], troff[NMB][2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hl);
+  perm_tr_offsets<D>(lane, troff);
+
   const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
-  const int sc = tid % CPR, sr0 = tid / CPR;
-  u32x4 kr[NPASS], vr[NPASS];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int kk = k0 + sr0 + i * RPP;
-      const u32x4 z = {0, 0, 0, 0};
-      kr[i] = kk < nk ? ld16(kbase + (long)kk * rs + 8 * sc) : z;
-      vr[i] = kk < nk ? ld16(vbase + (long)kk * rs + 8 * sc) : z;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = sr0 + i * RPP;
-      const int rk = (r & ~31) | kRowPerm(r & 31);
-      *reinterpret_cast<u32x4*>(&sK[buf][rk * KS + 8 * sc]) = kr[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][rk * KS + 8 * sc]) = vr[i];
-    }
+  auto issue = [&](int k0, int buf) {
+    const int last = nk - 1;
+    auto row = [&](int r) { return min(k0 + ((r & ~31) | kRowPerm(r & 31)), last); };
+    tile_load_async<D, BN, 4>(sm.k[buf], kbase, rs, row);
+    tile_load_async<D, BN, 4>(sm.v[buf], vbase, rs, row);
   };
   auto tile_valid = [&](int k0) -> uint64_t {
     const int kk = k0 + lane;
@@ -345,75 +334,71 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     return __ballot(ok);
   };
 
-  const int g = lane >> 4, src = lane & 15;
-  const int tr_off = (4 * (g >> 1) + (src >> 2)) * KS + 16 * (g & 1) + 4 * (src & 3);
-
   f32x16 dqacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
   const float c2 = p.c2;
 
+  auto compute = [&](auto masked, int buf, uint64_t vw) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const char* kt = sm.k[buf];
+    const char* vt = sm.v[buf];
+    uint32_t w2[2] = {0u, 0u};
+    if (MASKED) {
+      const uint64_t vl = vw >> (8 * hl);
+      w2[0] = (uint32_t)vl;
+      w2[1] = (uint32_t)(vl >> 32);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int rb = kb * 32 * RB;
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) st = mfma32(lds_row16(kt, rb + koff[ks]), qreg[ks], st);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) dpt = mfma32(lds_row16(vt, rb + koff[ks]), doreg[ks], dpt);
+      // Register r holds key 32*kb + 16*(r/8) + 8*hl + r%8 of the tile.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
+        if (MASKED) pr = (w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u ? pr : 0.f;
+        dpt[r] = pr * (dpt[r] - dl);
+      }
+      const bf16x8 ds0 = pack8(dpt, 0), ds1 = pack8(dpt, 8);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        dqacc[mb] = mfma32(lds_tr8(kt + rb, troff[mb][0], troff[mb][1]), ds0, dqacc[mb]);
+        dqacc[mb] = mfma32(lds_tr8(kt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds1, dqacc[mb]);
+      }
+    }
+  };
+
   const int ntiles = (nk + BN - 1) / BN;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  uint64_t vw = ntiles > 0 ? tile_valid(0) : 0;
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  uint64_t vw = 0;
+  auto step = [&](int j, int buf) {
     const bool more = j + 1 < ntiles;
     uint64_t vw_next = 0;
     if (more) {
-      load_tile((j + 1) * BN);
+      issue((j + 1) * BN, buf ^ 1);
       vw_next = tile_valid((j + 1) * BN);
     }
-    if (vw != 0) {
-      const bf16* sKb = sK[buf];
-      const bf16* sVb = sV[buf];
-      f32x16 st[2], dpt[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = f32x16{};
-        dpt[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sKb[(32 * kb + l32) * KS + 16 * ks + 8 * hl]);
-          st[kb] = mfma32(a, qreg[ks], st[kb]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sVb[(32 * kb + l32) * KS + 16 * ks + 8 * hl]);
-          dpt[kb] = mfma32(a, doreg[ks], dpt[kb]);
-        }
-      }
-      const bool full = vw == ~0ull;
-      bf16x8 dsk[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(st[kb][r], c2, -lse2));
-          if (!full && !((vw >> (32 * kb + c_row_permuted(r, hl))) & 1ull)) pr = 0.f;
-          dpt[kb][r] = pr * (dpt[kb][r] - dl);
-        }
-        dsk[kb][0] = pack8(dpt[kb], 0);
-        dsk[kb][1] = pack8(dpt[kb], 8);
-      }
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16* kp = sKb + (32 * kb + 16 * t) * KS + 32 * mb + tr_off;
-            const bf16x8 a = cat_tr(lds_read_tr16(kp), lds_read_tr16(kp + 8 * KS));
-            dqacc[mb] = mfma32(a, dsk[kb][t], dqacc[mb]);
-          }
-    }
-    if (more) store_tile(buf ^ 1);
+    if (vw == ~0ull)
+      compute(Flag<false>{}, buf, vw);
+    else if (vw != 0)
+      compute(Flag<true>{}, buf, vw);
+    wait_tile_loads();
     __syncthreads();
     vw = vw_next;
+  };
+  if (ntiles > 0) {
+    issue(0, 0);
+    vw = tile_valid(0);
+    wait_tile_loads();
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < ntiles) step(j + 1, 1);
   }
 
   if (qrow < nq) {
@@ -433,7 +418,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 // One launch for the whole backward.  Logical workgroup ids are grouped per
 // (outer, head): [dK/dV tiles of that head][dQ tiles of that head].
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_kernel(BwdParams p) {
   union Smem {
     DkdvSmem<D> kv;
     DqSmem<D> q;

@@ -10,34 +10,36 @@
 //    S^T = K Q^T, so the score tile arrives with one query per lane and all
 //    row statistics (max, sum, LSE) are per-lane values; the only cross-lane
 //    step is one exchange between the two 32-lane halves.
-//  * K/V tiles of 64 keys are double-buffered through LDS: the global loads of
-//    tile j+1 are in flight while tile j is consumed; one barrier per tile.
+//  * K/V tiles of 64 keys are double-buffered in LDS and filled asynchronously
+//    by global_load_lds (tile j+1 is in flight while tile j is consumed; one
+//    barrier per tile).  Tiles are unpadded and XOR-swizzled (tile.hpp) so the
+//    row reads of K and the transposing reads of V are bank-conflict free.
 //    K rows are stored permuted (kRowPerm) so that the exponentiated score
-//    registers are directly the B operand of O^T += V^T P^T; V^T comes from
-//    row-major V with the LDS transposing read.
+//    registers are directly the B operand of O^T += V^T P^T.
 //  * Online softmax in base 2 with scale*log2(e) folded into one FMA.  The
 //    running max is only moved (and O, l rescaled) when the new tile max
 //    exceeds it by more than 8 (log2 units), so the rescale is rare; the
 //    unnormalised weights stay below 2^8 and the final division uses the
 //    same reference max, so the result is the same softmax.
 //  * Tiles whose keys are all masked are skipped; partially valid tiles (a
-//    ragged tail or a mask edge) set the excluded scores to -inf.
+//    ragged tail or a mask edge) take a separate path that sets the excluded
+//    scores to -inf, so full tiles carry no per-element mask work.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile.hpp"
 
 namespace attn {
 
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KS = D + 8, VS = D + 8;  // LDS row strides (elements), 16 B of padding
-  constexpr int NKS = D / 16;            // MFMA reduction steps over the head dim
-  constexpr int NMB = D / 32;            // 32-row blocks of O^T
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;         // rows staged per pass
-  constexpr int NPASS = BN / RPP;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * VS];
+  constexpr int RB = 2 * D;       // tile row bytes
+  constexpr int NKS = D / 16;     // MFMA reduction steps over the head dim
+  constexpr int NMB = D / 32;     // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(1024))) char sK0[BN * RB];
+  __shared__ __attribute__((aligned(1024))) char sK1[BN * RB];
+  __shared__ __attribute__((aligned(1024))) char sV0[BN * RB];
+  __shared__ __attribute__((aligned(1024))) char sV1[BN * RB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -73,34 +75,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int qrow = qb + wave * 32 + l32;
   bf16x8 qreg[NKS];
   {
-    const bf16* qp = p.q + ((long)qrow0 + qrow) * rs + (long)head * D + 8 * hl;
+    const bf16* qp = p.q + ((long)qrow0 + min(qrow, nq - 1)) * rs + (long)head * D + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 z = {0, 0, 0, 0};
-      qreg[ks] = as_bf16x8(qrow < nq ? ld16(qp + 16 * ks) : z);
-    }
+    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = as_bf16x8(ld16(qp + 16 * ks));
   }
 
-  // Staging: thread -> (chunk c, rows r0 + i*RPP).
-  const int sc = tid % CPR, sr0 = tid / CPR;
-  u32x4 kr[NPASS], vr[NPASS];
-  auto load_tile = [&](int k0) {
+  // Per-lane swizzled LDS offsets: K rows (MFMA A operand, one row per lane) and the
+  // transposing V reads (lane group g, source lane src; see lds_read_tr16).
+  int koff[NKS], voff[NMB][2];
 #pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int key = k0 + sr0 + i * RPP;
-      const u32x4 z = {0, 0, 0, 0};
-      kr[i] = key < nk ? ld16(kbase + (long)key * rs + 8 * sc) : z;
-      vr[i] = key < nk ? ld16(vbase + (long)key * rs + 8 * sc) : z;
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hl);
+  {
+    const int g = lane >> 4, src = lane & 15;
 #pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = sr0 + i * RPP;
-      const int rk = (r & ~31) | kRowPerm(r & 31);
-      *reinterpret_cast<u32x4*>(&sK[buf][rk * KS + 8 * sc]) = kr[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][r * VS + 8 * sc]) = vr[i];
-    }
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        voff[mb][half] = tile_off_tr<D>(8 * (g >> 1) + 4 * half + (src >> 2),
+                                        32 * mb + 16 * (g & 1) + 4 * (src & 3));
+  }
+
+  auto issue = [&](int k0, char* kt, char* vt) {
+    const int last = nk - 1;
+    tile_load_async<D, BN, 4>(kt, kbase, rs, [&](int r) {
+      return min(k0 + ((r & ~31) | kRowPerm(r & 31)), last);
+    });
+    tile_load_async<D, BN, 4>(vt, vbase, rs, [&](int r) { return min(k0 + r, last); });
   };
   auto tile_valid = [&](int k0) -> uint64_t {
     const int key = k0 + lane;
@@ -109,96 +109,99 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     return __ballot(ok);
   };
 
-  // Per-lane offset of the transposing V read (see lds_read_tr16).
-  const int g = lane >> 4, src = lane & 15;
-  const int vt_off = (8 * (g >> 1) + (src >> 2)) * VS + 16 * (g & 1) + 4 * (src & 3);
-
   f32x16 oacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = p.c2;
 
-  const int ntiles = (nk + BN - 1) / BN;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  uint64_t vw = ntiles > 0 ? tile_valid(0) : 0;
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ntiles;
-    uint64_t vw_next = 0;
-    if (more) {
-      load_tile((j + 1) * BN);
-      vw_next = tile_valid((j + 1) * BN);
+  auto compute = [&](auto masked, const char* kt, const char* vt, uint64_t vw) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
     }
-    if (vw != 0) {
-      const bf16* sKb = sK[buf];
-      const bf16* sVb = sV[buf];
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sKb[(32 * kb + l32) * KS + 16 * ks + 8 * hl]);
-          sacc[kb] = mfma32(a, qreg[ks], sacc[kb]);
-        }
-      }
-      if (vw != ~0ull) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((vw >> (32 * kb + c_row_permuted(r, hl))) & 1ull)) sacc[kb][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
+    if (MASKED) {
+      // bit (32kb + 16(r/8) + 8hl + r%8) of vw is the validity of register r's key
+      const uint64_t vl = vw >> (8 * hl);
+      const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = wave_max_halves(mx);
-      const float mt = mx * c2;
-      if (__ballot(mt > m_run + 8.0f)) {
-        const float mnew = fmaxf(m_run, mt);
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-        l_run *= alpha;
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = (w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u ? sacc[kb][r] : -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-        m_run = mnew;
-      }
-      const float muse = m_run == -INFINITY ? 0.f : m_run;
-      bf16x8 pk[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -muse));
-          sacc[kb][r] = x;
-          l_run += x;
-        }
-        pk[kb][0] = pack8(sacc[kb], 0);
-        pk[kb][1] = pack8(sacc[kb], 8);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = wave_max_halves(mx);
+    const float mt = mx * c2;
+    if (__ballot(mt > m_run + 8.0f)) {
+      const float mnew = fmaxf(m_run, mt);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16* vp = sVb + (32 * kb + 16 * t) * VS + 32 * mb + vt_off;
-            const bf16x8 a = cat_tr(lds_read_tr16(vp), lds_read_tr16(vp + 4 * VS));
-            oacc[mb] = mfma32(a, pk[kb][t], oacc[mb]);
-          }
+        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+      m_run = mnew;
     }
-    if (more) store_tile(buf ^ 1);
+    const float muse = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pk[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -muse));
+        sacc[kb][r] = x;
+        l_run += x;
+      }
+      pk[kb][0] = pack8(sacc[kb], 0);
+      pk[kb][1] = pack8(sacc[kb], 8);
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const char* vb = vt + (32 * kb + 16 * t) * RB;
+          oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
+        }
+  };
+
+  const int ntiles = (nk + BN - 1) / BN;
+  uint64_t vw = 0;
+  auto step = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
+    const bool more = j + 1 < ntiles;
+    uint64_t vw_next = 0;
+    if (more) {
+      issue((j + 1) * BN, kn, vn);
+      vw_next = tile_valid((j + 1) * BN);
+    }
+    if (vw == ~0ull)
+      compute(Flag<false>{}, kt, vt, vw);
+    else if (vw != 0)
+      compute(Flag<true>{}, kt, vt, vw);
+    wait_tile_loads();
     __syncthreads();
     vw = vw_next;
+  };
+  if (ntiles > 0) {
+    issue(0, sK0, sV0);
+    vw = tile_valid(0);
+    wait_tile_loads();
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, sK0, sV0, sK1, sV1);
+    if (j + 1 < ntiles) step(j + 1, sK1, sV1, sK0, sV0);
   }
 
   l_run = wave_sum_halves(l_run);

@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=27280,
                     help="query rows of one head in the CPU-oracle sample")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known "
+                         "byte count for scaling the profiler's HBM counters)")
     return ap.parse_args()
 
 
@@ -156,6 +159,14 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_rows)
     print(json.dumps(res), flush=True)
