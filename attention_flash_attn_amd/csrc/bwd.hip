@@ -34,8 +34,8 @@
 // K/V tiles of 64 keys are double-buffered in LDS the same way; K^T comes from
 // the transposing read.
 //
-// Partial tiles (a ragged tail, a mask edge) take separate code paths, so full
-// tiles carry no per-element mask work.
+// Partial tiles (a ragged tail, a mask edge) zero the excluded weights in a
+// branch taken only there, so full tiles carry no per-element mask work.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -183,12 +183,13 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 
   const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.head * D;
   const bf16* obase = p.dout + (long)sl.qrow0 * rs + (long)sl.head * D;
+  auto qrow_of = [](int r) { return perm32_row(r); };
+  TileLoader<D, BQ, 4> ld;
+  ld.init(rs, qrow_of);
   float lr = 0.f, dl = 0.f;
   auto issue = [&](int q0, int buf) {
-    const int last = nq - 1;
-    auto row = [&](int r) { return min(q0 + ((r & ~31) | kRowPerm(r & 31)), last); };
-    tile_load_async<D, BQ, 4>(sm.q[buf], qbase, rs, row);
-    tile_load_async<D, BQ, 4>(sm.o[buf], obase, rs, row);
+    ld.issue(sm.q[buf], qbase, rs, q0, nq, qrow_of);
+    ld.issue(sm.o[buf], obase, rs, q0, nq, qrow_of);
     if (tid < BQ) {
       const int qi = q0 + tid;
       lr = qi < nq ? p.lse[sl.lse_base + qi] * kLog2e : INFINITY;
@@ -207,8 +208,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
   const float c2 = p.c2;
 
-  auto compute = [&](auto masked, int buf) {
-    constexpr bool MASKED = decltype(masked)::value;
+  const bool all_keys = kball == ~0ull;
+  auto compute = [&](int buf) {
     const char* qt = sm.q[buf];
     const char* ot = sm.o[buf];
 #pragma unroll
@@ -227,12 +228,14 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
       const f32x4 D0 = *reinterpret_cast<const f32x4*>(Dp), D1 = *reinterpret_cast<const f32x4*>(Dp + 4);
       const f32x4 D2 = *reinterpret_cast<const f32x4*>(Dp + 16), D3 = *reinterpret_cast<const f32x4*>(Dp + 20);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r)));
-        if (MASKED) pr = kvalid ? pr : 0.f;
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - pick16(D0, D1, D2, D3, r));
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r)));
+      if (!all_keys) {
+        keep_branch();  // keys past the end or masked out: P = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = kvalid ? s[r] : 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - pick16(D0, D1, D2, D3, r));
       const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
       const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
 #pragma unroll
@@ -249,10 +252,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   auto step = [&](int j, int buf) {
     const bool more = j + 1 < ntiles;
     if (more) issue((j + 1) * BQ, buf ^ 1);
-    if (kball == ~0ull)
-      compute(Flag<false>{}, buf);
-    else if (kball != 0)
-      compute(Flag<true>{}, buf);
+    if (kball != 0) compute(buf);
     if (more) publish_stats(buf ^ 1);
     wait_tile_loads();
     __syncthreads();
@@ -321,11 +321,12 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 
   const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
+  auto krow_of = [](int r) { return perm32_row(r); };
+  TileLoader<D, BN, 4> ld;
+  ld.init(rs, krow_of);
   auto issue = [&](int k0, int buf) {
-    const int last = nk - 1;
-    auto row = [&](int r) { return min(k0 + ((r & ~31) | kRowPerm(r & 31)), last); };
-    tile_load_async<D, BN, 4>(sm.k[buf], kbase, rs, row);
-    tile_load_async<D, BN, 4>(sm.v[buf], vbase, rs, row);
+    ld.issue(sm.k[buf], kbase, rs, k0, nk, krow_of);
+    ld.issue(sm.v[buf], vbase, rs, k0, nk, krow_of);
   };
   auto tile_valid = [&](int k0) -> uint64_t {
     const int kk = k0 + lane;
@@ -339,16 +340,11 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
   const float c2 = p.c2;
 
-  auto compute = [&](auto masked, int buf, uint64_t vw) {
-    constexpr bool MASKED = decltype(masked)::value;
+  auto compute = [&](int buf, uint64_t vw) {
     const char* kt = sm.k[buf];
     const char* vt = sm.v[buf];
-    uint32_t w2[2] = {0u, 0u};
-    if (MASKED) {
-      const uint64_t vl = vw >> (8 * hl);
-      w2[0] = (uint32_t)vl;
-      w2[1] = (uint32_t)(vl >> 32);
-    }
+    const uint64_t vl = vw >> (8 * hl);
+    const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int rb = kb * 32 * RB;
@@ -359,11 +355,14 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       for (int ks = 0; ks < NKS; ++ks) dpt = mfma32(lds_row16(vt, rb + koff[ks]), doreg[ks], dpt);
       // Register r holds key 32*kb + 16*(r/8) + 8*hl + r%8 of the tile.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
-        if (MASKED) pr = (w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u ? pr : 0.f;
-        dpt[r] = pr * (dpt[r] - dl);
+      for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
+      if (vw != ~0ull) {
+        keep_branch();  // partial tile: register r's key is bit 32kb + 16(r/8) + 8hl + r%8
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = (w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u ? st[r] : 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dl);
       const bf16x8 ds0 = pack8(dpt, 0), ds1 = pack8(dpt, 8);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
@@ -382,10 +381,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       issue((j + 1) * BN, buf ^ 1);
       vw_next = tile_valid((j + 1) * BN);
     }
-    if (vw == ~0ull)
-      compute(Flag<false>{}, buf, vw);
-    else if (vw != 0)
-      compute(Flag<true>{}, buf, vw);
+    if (vw != 0) compute(buf, vw);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;

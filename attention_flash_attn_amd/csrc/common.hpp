@@ -80,7 +80,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
-__device__ __forceinline__ float wave_max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32); }
+// Placed first in a rarely taken, wave-uniform branch: an empty volatile asm has
+// side effects, so the compiler keeps the branch instead of flattening its body
+// into selects executed on every iteration.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// Reductions over lane pairs (l, l^32), i.e. the two halves of a wave, with
+// v_permlane32_swap on two copies of x: the swapped pair holds x[l%32] and
+// x[l%32 + 32] in every lane l.
+__device__ __forceinline__ float wave_max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace attn

@@ -21,8 +21,8 @@
 //    exceeds it by more than 8 (log2 units), so the rescale is rare; the
 //    unnormalised weights stay below 2^8 and the final division uses the
 //    same reference max, so the result is the same softmax.
-//  * Tiles whose keys are all masked are skipped; partially valid tiles (a
-//    ragged tail or a mask edge) take a separate path that sets the excluded
+//  * Tiles whose keys are all masked are skipped; in partially valid tiles (a
+//    ragged tail or a mask edge) a branch taken only there sets the excluded
 //    scores to -inf, so full tiles carry no per-element mask work.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -95,12 +95,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                                         32 * mb + 16 * (g & 1) + 4 * (src & 3));
   }
 
+  TileLoader<D, BN, 4> kld, vld;
+  auto krow = [](int r) { return perm32_row(r); };
+  auto vrow = [](int r) { return r; };
+  kld.init(rs, krow);
+  vld.init(rs, vrow);
   auto issue = [&](int k0, char* kt, char* vt) {
-    const int last = nk - 1;
-    tile_load_async<D, BN, 4>(kt, kbase, rs, [&](int r) {
-      return min(k0 + ((r & ~31) | kRowPerm(r & 31)), last);
-    });
-    tile_load_async<D, BN, 4>(vt, vbase, rs, [&](int r) { return min(k0 + r, last); });
+    kld.issue(kt, kbase, rs, k0, nk, krow);
+    vld.issue(vt, vbase, rs, k0, nk, vrow);
   };
   auto tile_valid = [&](int k0) -> uint64_t {
     const int key = k0 + lane;
@@ -115,8 +117,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = p.c2;
 
-  auto compute = [&](auto masked, const char* kt, const char* vt, uint64_t vw) {
-    constexpr bool MASKED = decltype(masked)::value;
+  auto compute = [&](const char* kt, const char* vt, uint64_t vw) {
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -125,8 +126,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       for (int ks = 0; ks < NKS; ++ks)
         sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
     }
-    if (MASKED) {
-      // bit (32kb + 16(r/8) + 8hl + r%8) of vw is the validity of register r's key
+    if (vw != ~0ull) {
+      keep_branch();
+      // Partial tile.  Bit (32kb + 16(r/8) + 8hl + r%8) of vw is register r's key.
       const uint64_t vl = vw >> (8 * hl);
       const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
 #pragma unroll
@@ -143,6 +145,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     mx = wave_max_halves(mx);
     const float mt = mx * c2;
     if (__ballot(mt > m_run + 8.0f)) {
+      keep_branch();
       const float mnew = fmaxf(m_run, mt);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
       l_run *= alpha;
@@ -185,10 +188,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       issue((j + 1) * BN, kn, vn);
       vw_next = tile_valid((j + 1) * BN);
     }
-    if (vw == ~0ull)
-      compute(Flag<false>{}, kt, vt, vw);
-    else if (vw != 0)
-      compute(Flag<true>{}, kt, vt, vw);
+    if (vw != 0) compute(kt, vt, vw);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;

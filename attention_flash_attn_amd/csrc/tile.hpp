@@ -51,31 +51,56 @@ __device__ __forceinline__ bf16x8 lds_tr8(const char* tile, int off_lo, int off_
                 lds_read_tr16(reinterpret_cast<const bf16*>(tile + off_hi)));
 }
 
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
+// Asynchronous tile copy with NW waves.  Lane-dependent parts of the global
+// addresses are fixed per kernel, so they are computed once: off[i] is the byte
+// offset, from the global address of the tile's first row, of the 16-byte chunk
+// this lane fetches with its i-th instruction.  row_of(r) maps tile row r to its
+// row offset within the tile (a permutation of 0..ROWS-1).  A tile that runs past
+// the last valid row re-reads that row instead (a tail tile only).
+template <int D, int ROWS, int NW>
+struct TileLoader {
+  static constexpr int CPR = D / 8;            // chunks per row
+  static constexpr int RPI = 1024 / (2 * D);   // rows per instruction (4 or 8)
+  static constexpr int NI = ROWS * 2 * D / 1024 / NW;
+  static_assert(ROWS * 2 * D % (1024 * NW) == 0, "tile must split evenly over the waves");
+  uint32_t off[NI];
+
+  template <typename RowOf>
+  __device__ __forceinline__ void init(long rs, RowOf row_of) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave + i * NW) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(r);
+      off[i] = (uint32_t)(2 * ((long)row_of(r) * rs + 8 * c));
+    }
+  }
+
+  // Copy rows [row0, row0 + ROWS) of the tensor whose row 0 (this head) is at `base`;
+  // only rows < nrows exist.
+  template <typename RowOf>
+  __device__ __forceinline__ void issue(char* tile, const bf16* base, long rs, int row0, int nrows,
+                                        RowOf row_of) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const char* g = reinterpret_cast<const char*>(base + (long)row0 * rs);
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        __builtin_amdgcn_global_load_lds(g + off[i], (lds_void*)(tile + (wave + i * NW) * 1024), 16, 0, 0);
+    } else {
+      const int lane = threadIdx.x & 63, last = nrows - 1 - row0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = (wave + i * NW) * RPI + lane / CPR;
+        const int want = row_of(r), have = min(want, last);
+        const long o = (long)off[i] + 2 * (long)(have - want) * rs;
+        __builtin_amdgcn_global_load_lds(g + o, (lds_void*)(tile + (wave + i * NW) * 1024), 16, 0, 0);
+      }
+    }
+  }
 };
 
-// Asynchronously copy ROWS tile rows into `tile` with NW waves.  row_src(r) gives the
-// global row index (already clamped into the tensor) holding tile row r; gbase points
-// at (row 0, this head), rs is the row stride in elements.
-template <int D, int ROWS, int NW, typename RowSrc>
-__device__ __forceinline__ void tile_load_async(char* tile, const bf16* gbase, long rs, RowSrc row_src) {
-  constexpr int CPR = D / 8;               // chunks per row
-  constexpr int RPI = 1024 / (2 * D);      // rows per instruction (4 or 8)
-  constexpr int NINST = ROWS * 2 * D / 1024;
-  static_assert(NINST % NW == 0, "tile must split evenly over the waves");
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = 0; i < NINST / NW; ++i) {
-    const int j = wave + i * NW;
-    const int r = j * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz<D>(r);
-    const bf16* src = gbase + (long)row_src(r) * rs + 8 * c;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + j * 1024), 16, 0, 0);
-  }
-}
+__device__ __forceinline__ int perm32_row(int r) { return (r & ~31) | kRowPerm(r & 31); }
 
 // Wait until this wave's asynchronous tile copies have landed.
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
