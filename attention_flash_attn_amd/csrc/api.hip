@@ -6,7 +6,7 @@
 #include <math.h>
 #include <limits.h>
 
-#include "../../include/libattn.h"
+#include "libattn.h"
 #include "common.hpp"
 #include "kernels.hpp"
 

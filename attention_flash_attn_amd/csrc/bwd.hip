@@ -187,19 +187,19 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   TileLoader<D, BQ, 4> ld;
   ld.init(rs, qrow_of);
   float lr = 0.f, dl = 0.f;
-  auto issue = [&](int q0, int buf) {
-    ld.issue(sm.q[buf], qbase, rs, q0, nq, qrow_of);
-    ld.issue(sm.o[buf], obase, rs, q0, nq, qrow_of);
+  auto issue = [&](int q0, char* qt, char* ot) {
+    ld.issue(qt, qbase, rs, q0, nq, qrow_of);
+    ld.issue(ot, obase, rs, q0, nq, qrow_of);
     if (tid < BQ) {
       const int qi = q0 + tid;
       lr = qi < nq ? p.lse[sl.lse_base + qi] * kLog2e : INFINITY;
       dl = qi < nq ? p.delta[sl.lse_base + qi] : 0.f;
     }
   };
-  auto publish_stats = [&](int buf) {
+  auto publish_stats = [&](float* lt, float* dt) {
     if (tid < BQ) {
-      sm.l[buf][tid] = lr;
-      sm.d[buf][tid] = dl;
+      lt[tid] = lr;
+      dt[tid] = dl;
     }
   };
 
@@ -208,64 +208,89 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
   const float c2 = p.c2;
 
-  const bool all_keys = kball == ~0ull;
-  auto compute = [&](int buf) {
-    const char* qt = sm.q[buf];
-    const char* ot = sm.o[buf];
+  // Three phases per 32-query sub-tile: scores A (S, dP MFMAs), weights B (VALU: P,
+  // dS), gradients C (dV, dK MFMAs).  They are issued as A0 | A1 B0 | C0 B1 | C1, with
+  // hard scheduling boundaries between the groups, so that each VALU phase sits in
+  // one scheduling region with independent MFMAs.  No masking is needed here: with
+  // one key per lane, P and dS of an excluded key only reach that key's own dK/dV
+  // accumulators, which are written as zeros at the end.
+  auto scores = [&](const char* qt, const char* ot, int sub, f32x16& s, f32x16& dp) {
+    const int rb = sub * 32 * RB;
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-    for (int sub = 0; sub < BQ / 32; ++sub) {
-      const int rb = sub * 32 * RB;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks) s = mfma32(lds_row16(qt, rb + qoff[ks]), kreg[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s = mfma32(lds_row16(qt, rb + qoff[ks]), kreg[ks], s);
+    for (int ks = 0; ks < NKS; ++ks) dp = mfma32(lds_row16(ot, rb + qoff[ks]), vreg[ks], dp);
+  };
+  auto weights = [&](const float* lt, const float* dt, int sub, f32x16& s, f32x16& dp,
+                     bf16x8 (&pk)[2], bf16x8 (&ds)[2]) {
+    // Register r holds query 32*sub + 16*(r/8) + 8*hl + r%8 of the tile.
+    const float* Lp = lt + 32 * sub + 8 * hl;
+    const float* Dp = dt + 32 * sub + 8 * hl;
+    const f32x4 L0 = *reinterpret_cast<const f32x4*>(Lp), L1 = *reinterpret_cast<const f32x4*>(Lp + 4);
+    const f32x4 L2 = *reinterpret_cast<const f32x4*>(Lp + 16), L3 = *reinterpret_cast<const f32x4*>(Lp + 20);
+    const f32x4 D0 = *reinterpret_cast<const f32x4*>(Dp), D1 = *reinterpret_cast<const f32x4*>(Dp + 4);
+    const f32x4 D2 = *reinterpret_cast<const f32x4*>(Dp + 16), D3 = *reinterpret_cast<const f32x4*>(Dp + 20);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) dp = mfma32(lds_row16(ot, rb + qoff[ks]), vreg[ks], dp);
-      // Register r holds query 32*sub + 16*(r/8) + 8*hl + r%8 of the tile.
-      const float* Lp = &sm.l[buf][32 * sub + 8 * hl];
-      const float* Dp = &sm.d[buf][32 * sub + 8 * hl];
-      const f32x4 L0 = *reinterpret_cast<const f32x4*>(Lp), L1 = *reinterpret_cast<const f32x4*>(Lp + 4);
-      const f32x4 L2 = *reinterpret_cast<const f32x4*>(Lp + 16), L3 = *reinterpret_cast<const f32x4*>(Lp + 20);
-      const f32x4 D0 = *reinterpret_cast<const f32x4*>(Dp), D1 = *reinterpret_cast<const f32x4*>(Dp + 4);
-      const f32x4 D2 = *reinterpret_cast<const f32x4*>(Dp + 16), D3 = *reinterpret_cast<const f32x4*>(Dp + 20);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r)));
-      if (!all_keys) {
-        keep_branch();  // keys past the end or masked out: P = 0
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = kvalid ? s[r] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - pick16(D0, D1, D2, D3, r));
-      const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
-      const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        dvacc[mb] = mfma32(lds_tr8(ot + rb, troff[mb][0], troff[mb][1]), pk0, dvacc[mb]);
-        dvacc[mb] = mfma32(lds_tr8(ot + rb + 16 * RB, troff[mb][0], troff[mb][1]), pk1, dvacc[mb]);
-        dkacc[mb] = mfma32(lds_tr8(qt + rb, troff[mb][0], troff[mb][1]), ds0, dkacc[mb]);
-        dkacc[mb] = mfma32(lds_tr8(qt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds1, dkacc[mb]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r)));
+      dp[r] = s[r] * (dp[r] - pick16(D0, D1, D2, D3, r));
     }
+    pk[0] = pack8(s, 0);
+    pk[1] = pack8(s, 8);
+    ds[0] = pack8(dp, 0);
+    ds[1] = pack8(dp, 8);
+  };
+  auto grads = [&](const char* qt, const char* ot, int sub, const bf16x8 (&pk)[2], const bf16x8 (&ds)[2]) {
+    const int rb = sub * 32 * RB;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      dvacc[mb] = mfma32(lds_tr8(ot + rb, troff[mb][0], troff[mb][1]), pk[0], dvacc[mb]);
+      dvacc[mb] = mfma32(lds_tr8(ot + rb + 16 * RB, troff[mb][0], troff[mb][1]), pk[1], dvacc[mb]);
+      dkacc[mb] = mfma32(lds_tr8(qt + rb, troff[mb][0], troff[mb][1]), ds[0], dkacc[mb]);
+      dkacc[mb] = mfma32(lds_tr8(qt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds[1], dkacc[mb]);
+    }
+  };
+  static_assert(BQ == 64, "the phase order below assumes two sub-tiles");
+  auto compute = [&](const char* qt, const char* ot, const float* lt, const float* dt) {
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pk0[2], ds0[2], pk1[2], ds1[2];
+    // Scheduling regions: A0 | A1 B0 | C0 B1 | C1 (each pair is independent work).
+    scores(qt, ot, 0, s0, dp0);
+    __builtin_amdgcn_sched_barrier(0);
+    scores(qt, ot, 1, s1, dp1);
+    weights(lt, dt, 0, s0, dp0, pk0, ds0);
+    __builtin_amdgcn_sched_barrier(0);
+    grads(qt, ot, 0, pk0, ds0);
+    weights(lt, dt, 1, s1, dp1, pk1, ds1);
+    __builtin_amdgcn_sched_barrier(0);
+    grads(qt, ot, 1, pk1, ds1);
   };
 
   const int ntiles = (nq + BQ - 1) / BQ;
-  auto step = [&](int j, int buf) {
+  // The current and the next tile's buffers are distinct __restrict__ parameters, so
+  // once inlined the compiler can tell reads of one from the asynchronous copy into
+  // the other (without that it waits for the copy before the first LDS read).
+  auto step = [&](int j, const char* __restrict__ cq, const char* __restrict__ co,
+                  const float* __restrict__ cl, const float* __restrict__ cd, char* __restrict__ nq_,
+                  char* __restrict__ no_, float* __restrict__ nl, float* __restrict__ nd) {
     const bool more = j + 1 < ntiles;
-    if (more) issue((j + 1) * BQ, buf ^ 1);
-    if (kball != 0) compute(buf);
-    if (more) publish_stats(buf ^ 1);
+    if (more) issue((j + 1) * BQ, nq_, no_);
+    if (kball != 0) compute(cq, co, cl, cd);
+    if (more) publish_stats(nl, nd);
     wait_tile_loads();
     __syncthreads();
   };
   if (ntiles > 0) {
-    issue(0, 0);
-    publish_stats(0);
+    issue(0, sm.q[0], sm.o[0]);
+    publish_stats(sm.l[0], sm.d[0]);
     wait_tile_loads();
   }
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, 0);
-    if (j + 1 < ntiles) step(j + 1, 1);
+    step(j, sm.q[0], sm.o[0], sm.l[0], sm.d[0], sm.q[1], sm.o[1], sm.l[1], sm.d[1]);
+    if (j + 1 < ntiles) step(j + 1, sm.q[1], sm.o[1], sm.l[1], sm.d[1], sm.q[0], sm.o[0], sm.l[0], sm.d[0]);
   }
 
   if (key < nk) {
@@ -277,8 +302,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
         bf16x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = (bf16)(dkacc[mb][4 * j4 + e] * p.scale);
-          b[e] = (bf16)dvacc[mb][4 * j4 + e];
+          a[e] = (bf16)(kvalid ? dkacc[mb][4 * j4 + e] * p.scale : 0.f);
+          b[e] = (bf16)(kvalid ? dvacc[mb][4 * j4 + e] : 0.f);
         }
         *reinterpret_cast<bf16x4*>(p.dk + off + 32 * mb + 8 * j4) = a;
         *reinterpret_cast<bf16x4*>(p.dv + off + 32 * mb + 8 * j4) = b;
@@ -324,9 +349,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   auto krow_of = [](int r) { return perm32_row(r); };
   TileLoader<D, BN, 4> ld;
   ld.init(rs, krow_of);
-  auto issue = [&](int k0, int buf) {
-    ld.issue(sm.k[buf], kbase, rs, k0, nk, krow_of);
-    ld.issue(sm.v[buf], vbase, rs, k0, nk, krow_of);
+  auto issue = [&](int k0, char* kt, char* vt) {
+    ld.issue(kt, kbase, rs, k0, nk, krow_of);
+    ld.issue(vt, vbase, rs, k0, nk, krow_of);
   };
   auto tile_valid = [&](int k0) -> uint64_t {
     const int kk = k0 + lane;
@@ -340,61 +365,88 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
   const float c2 = p.c2;
 
-  auto compute = [&](int buf, uint64_t vw) {
-    const char* kt = sm.k[buf];
-    const char* vt = sm.v[buf];
-    const uint64_t vl = vw >> (8 * hl);
-    const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
+  // Per 32-key half kb of a tile: scores A (S^T, dP^T MFMAs), weights B (VALU: P,
+  // dS), gradient C (dQ^T MFMAs), issued as A0 | A1 B0 | C0 B1 | C1 with hard
+  // scheduling boundaries.  Partial tiles mask the scores (to -inf) between the groups.
+  auto scores = [&](const char* kt, const char* vt, int kb, f32x16& st, f32x16& dpt) {
+    const int rb = kb * 32 * RB;
+    st = f32x16{};
+    dpt = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int rb = kb * 32 * RB;
-      f32x16 st = f32x16{}, dpt = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks) st = mfma32(lds_row16(kt, rb + koff[ks]), qreg[ks], st);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) st = mfma32(lds_row16(kt, rb + koff[ks]), qreg[ks], st);
+    for (int ks = 0; ks < NKS; ++ks) dpt = mfma32(lds_row16(vt, rb + koff[ks]), doreg[ks], dpt);
+  };
+  auto mask_scores = [&](uint64_t vw, int kb, f32x16& st) {
+    // register r's key is bit 32kb + 16(r/8) + 8hl + r%8 of vw
+    const uint32_t w = (uint32_t)((vw >> (8 * hl)) >> (32 * kb));
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) dpt = mfma32(lds_row16(vt, rb + koff[ks]), doreg[ks], dpt);
-      // Register r holds key 32*kb + 16*(r/8) + 8*hl + r%8 of the tile.
+    for (int r = 0; r < 16; ++r) st[r] = (w >> (16 * (r >> 3) + (r & 7))) & 1u ? st[r] : -INFINITY;
+  };
+  auto weights = [&](f32x16& st, f32x16& dpt, bf16x8 (&ds)[2]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
-      if (vw != ~0ull) {
-        keep_branch();  // partial tile: register r's key is bit 32kb + 16(r/8) + 8hl + r%8
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = (w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u ? st[r] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dl);
-      const bf16x8 ds0 = pack8(dpt, 0), ds1 = pack8(dpt, 8);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        dqacc[mb] = mfma32(lds_tr8(kt + rb, troff[mb][0], troff[mb][1]), ds0, dqacc[mb]);
-        dqacc[mb] = mfma32(lds_tr8(kt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds1, dqacc[mb]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
+      dpt[r] = st[r] * (dpt[r] - dl);
     }
+    ds[0] = pack8(dpt, 0);
+    ds[1] = pack8(dpt, 8);
+  };
+  auto grad = [&](const char* kt, int kb, const bf16x8 (&ds)[2]) {
+    const int rb = kb * 32 * RB;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      dqacc[mb] = mfma32(lds_tr8(kt + rb, troff[mb][0], troff[mb][1]), ds[0], dqacc[mb]);
+      dqacc[mb] = mfma32(lds_tr8(kt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds[1], dqacc[mb]);
+    }
+  };
+  auto compute = [&](const char* kt, const char* vt, uint64_t vw) {
+    f32x16 st0, dpt0, st1, dpt1;
+    bf16x8 ds0[2], ds1[2];
+    scores(kt, vt, 0, st0, dpt0);
+    if (vw != ~0ull) {
+      keep_branch();
+      mask_scores(vw, 0, st0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    scores(kt, vt, 1, st1, dpt1);
+    weights(st0, dpt0, ds0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (vw != ~0ull) {
+      keep_branch();
+      mask_scores(vw, 1, st1);
+    }
+    grad(kt, 0, ds0);
+    weights(st1, dpt1, ds1);
+    __builtin_amdgcn_sched_barrier(0);
+    grad(kt, 1, ds1);
   };
 
   const int ntiles = (nk + BN - 1) / BN;
   uint64_t vw = 0;
-  auto step = [&](int j, int buf) {
+  // Current and next tile buffers as distinct __restrict__ parameters (see dkdv_block).
+  auto step = [&](int j, const char* __restrict__ ck, const char* __restrict__ cv,
+                  char* __restrict__ nk_, char* __restrict__ nv) {
     const bool more = j + 1 < ntiles;
     uint64_t vw_next = 0;
     if (more) {
-      issue((j + 1) * BN, buf ^ 1);
+      issue((j + 1) * BN, nk_, nv);
       vw_next = tile_valid((j + 1) * BN);
     }
-    if (vw != 0) compute(buf, vw);
+    if (vw != 0) compute(ck, cv, vw);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;
   };
   if (ntiles > 0) {
-    issue(0, 0);
+    issue(0, sm.k[0], sm.v[0]);
     vw = tile_valid(0);
     wait_tile_loads();
   }
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, 0);
-    if (j + 1 < ntiles) step(j + 1, 1);
+    step(j, sm.k[0], sm.v[0], sm.k[1], sm.v[1]);
+    if (j + 1 < ntiles) step(j + 1, sm.k[1], sm.v[1], sm.k[0], sm.v[0]);
   }
 
   if (qrow < nq) {

@@ -181,7 +181,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   const int ntiles = (nk + BN - 1) / BN;
   uint64_t vw = 0;
-  auto step = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
+  // Current and next tile buffers as distinct __restrict__ parameters: once inlined,
+  // the compiler can tell reads of one from the asynchronous copy into the other
+  // (without that it waits for the copy before the first LDS read).
+  auto step = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt,
+                  char* __restrict__ kn, char* __restrict__ vn) {
     const bool more = j + 1 < ntiles;
     uint64_t vw_next = 0;
     if (more) {
