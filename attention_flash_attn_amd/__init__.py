@@ -182,8 +182,19 @@ def attn_bwd(q, k, v, lse, delta, dout, key_mask=None, scale=None, dq=None, dk=N
 
 
 def _cu_args(cu_seqlens, device):
-    """Host int32 copy (validated by the library) and a device copy of cu_seqlens."""
+    """Host int32 copy (validated by the library) and a device copy of cu_seqlens.
+
+    Accepts one array (host or device; the other copy is made here) or a
+    (host_int32_tensor, device_int32_tensor) pair holding the same values, which
+    avoids any copy per call."""
     torch = _torch()
+    if isinstance(cu_seqlens, tuple) and len(cu_seqlens) == 2:
+        host, dev = cu_seqlens
+        if (host.device.type != "cpu" or host.dtype != torch.int32 or not host.is_contiguous()
+                or not dev.is_cuda or dev.dtype != torch.int32 or not dev.is_contiguous()
+                or host.numel() != dev.numel()):
+            raise ValueError("cu_seqlens pair must be (host int32, device int32) of equal length")
+        return host, dev
     cu = torch.as_tensor(cu_seqlens)
     host = cu.detach().to("cpu", torch.int32).contiguous()
     dev = cu if (cu.is_cuda and cu.dtype == torch.int32 and cu.is_contiguous()) else host.to(device)

@@ -91,8 +91,9 @@ template <bool VARLEN>
 __device__ __forceinline__ Slice decode(const BwdParams& p, int group, int tile) {
   Slice s;
   s.tile = tile;
-  s.head = group % p.H;
-  const int outer = group / p.H;
+  // head-major groups: equal work per XCD range when sequences differ (see fwd.hip)
+  s.head = group / p.B;
+  const int outer = group % p.B;
   s.mask = nullptr;
   if (VARLEN) {
     const int s0 = p.cu[outer], s1 = p.cu[outer + 1];

@@ -47,7 +47,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int logical = xcd_remap(blockIdx.x, p.n_blocks);
   const int qt = logical % p.n_qtiles;
   const int rest = logical / p.n_qtiles;
-  const int head = rest % p.H, outer = rest / p.H;
+  // (outer, head) groups go head-major: each XCD's contiguous range of groups then holds
+  // every batch|sequence of a few heads, so the ranges carry equal work even when the
+  // sequences differ in length (varlen) or in valid keys (mask).
+  const int head = rest / p.B, outer = rest % p.B;
   int qrow0, krow0, nq, nk;
   long lse_base;
   const uint8_t* mask = nullptr;

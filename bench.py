@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan_shard")
+    ap.add_argument("--workload", default="wan_shard",
+                    help="wan_shard (the metric's workload) or another named workload: "
+                         "probe_hs16, dit_s1024, mask_s4096, varlen4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=27280,
                     help="query rows of one head in the CPU-oracle sample")
@@ -44,6 +46,45 @@ def parse():
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling the profiler's HBM counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wan_shard_hbm_traffic.json")
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources; HBM counters recorded for another hash are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "attention_flash_attn_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when it was taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if workload != "wan_shard" or rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = {"attn_fwd": "fwd", "attn_bwd": "bwd"}[kernel]
+    return rec["kernels"][k]["hbm_bytes_per_launch"]
+
+
+def describe(w):
+    if w.name == "wan_shard":
+        return (f"wan_shard: B={w.B} N={w.S} H={w.H} D={w.D}, BSHD bf16, non-causal, no mask "
+                "(one Ulysses rank of the 40-head Wan layer)")
+    if w.varlen:
+        return f"{w.name}: packed varlen lengths {list(w.seqlens)} H={w.H} D={w.D}, bf16, non-causal"
+    m = f"key mask valid lengths {list(w.valid_lens)}" if w.valid_lens else "no mask"
+    return f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}, BSHD bf16, non-causal, {m}"
 
 
 def cpu_baseline(w, t, rows):
@@ -85,28 +126,42 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     A.lib()
     w = I.WORKLOADS[args.workload]
-    assert not w.varlen and w.valid_lens is None, "bench times the dense unmasked workload"
     t = I.draw_workload(w)
     dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = (dev(x) for x in (t.q, t.k, t.v, t.do))
     B, S, H, D = w.B, w.S, w.H, w.D
     out = torch.empty_like(q)
-    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-    delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    mask = None if t.key_mask is None else torch.from_numpy(t.key_mask).cuda()
+    if w.varlen:
+        T = w.T
+        lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        delta = torch.empty((1, H, T), dtype=torch.float32, device="cuda")
+        cu_host = torch.from_numpy(t.cu_seqlens)
+        cu_dev = cu_host.cuda()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        A.attn_fwd(q, k, v, None, None, out=out, lse=lse)
+        if w.varlen:
+            A.attn_varlen_fwd(q, k, v, (cu_host, cu_dev), None, out=out, lse=lse)
+        else:
+            A.attn_fwd(q, k, v, mask, None, out=out, lse=lse)
         if ev is not None:
             ev[1].record()
         A.attn_bwd_preprocess(out, do, delta=delta)
         if ev is not None:
             ev[2].record()
-        A.attn_bwd(q, k, v, lse, delta, do, None, None, dq=dq, dk=dk, dv=dv)
+        if w.varlen:
+            A.attn_varlen_bwd(q, k, v, lse, delta, do, (cu_host, cu_dev), None, dq=dq, dk=dk, dv=dv)
+        else:
+            A.attn_bwd(q, k, v, lse, delta, do, mask, None, dq=dq, dk=dk, dv=dv)
         if ev is not None:
             ev[3].record()
+
+    if not w.varlen:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+        delta = torch.empty_like(lse)
 
     for _ in range(args.warmup):
         step()
@@ -146,9 +201,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: q,k,v,dO ~ N(0,1) seed 4, rounded to bf16",
-        "config": {"workload": f"{w.name}: B={B} N={S} H={H} D={D}, BSHD bf16, non-causal, "
-                               "no mask (one Ulysses rank of the 40-head Wan layer)",
-                   "batch": B, "seq_len": S, "heads": H, "head_dim": D, "parallelism": "none"},
+        "config": {"workload": describe(w), "batch": B, "seq_len": S, "heads": H,
+                   "head_dim": D, "parallelism": "none"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"attn_fwd": round(fwd_ms, 4), "attn_bwd_preprocess": round(pre_ms, 4),
                        "attn_bwd": round(bwd_ms, 4)},
@@ -157,7 +211,8 @@ def main():
         "wall_ms_per_step": round(1e3 * wall / K, 4),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name, dom)},
     }
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
@@ -167,8 +222,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_rows)
+    if not args.no_cpu_baseline and not w.varlen and w.valid_lens is None:
+        res["cpu_baseline"] = cpu_baseline(w, t, min(args.cpu_rows, w.S))
     print(json.dumps(res), flush=True)
 
 
