@@ -18,7 +18,9 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
-bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+// The backward starts its score accumulators from -LSE/scale; the lower bound keeps that
+// finite for any LSE the forward can produce.
+bool scale_ok(float s) { return isfinite(s) && s >= 0x1p-64f; }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 // A tensor pointer may be NULL only when the tensor has no elements.

@@ -14,25 +14,28 @@
 // dK/dV and dQ come from two kernels that each own their output rows, so
 // there are no atomics and the result is bitwise reproducible.
 //
-// dK/dV kernel: one workgroup = 4 waves = 128 keys; each wave keeps its 32
-// keys' K and V rows in registers (B operands of S = Q K^T and dP = dO V^T,
-// so the score tile has one key per lane) and its dK^T, dV^T accumulators in
-// registers across the whole loop over query tiles.  Query tiles of 64 rows
-// (Q, dO, LSE, delta) are double-buffered in LDS, filled asynchronously by
-// global_load_lds into XOR-swizzled rows (tile.hpp); Q^T and dO^T operands come
-// from the LDS transposing read.
+// dK/dV workgroup: 8 waves, 128 keys.  The keys' K and V rows sit in LDS for the whole
+// loop; query tiles of 64 rows (Q, dO, LSE, delta) are double-buffered in LDS, filled
+// asynchronously by global_load_lds into XOR-swizzled rows (tile.hpp).  Wave w owns key
+// block w%4 (32 keys, one per lane of the score tile S = Q K^T) and query sub-tile w/4 of
+// every tile, with its dK^T, dV^T accumulators in registers across the loop; the two
+// waves of a key block add their partial sums through LDS at the end.  Q^T and dO^T
+// operands come from the LDS transposing read.
+//
+// dQ workgroup: 8 waves, 256 query rows; each wave keeps its 32 rows of Q and dO (B
+// operands of S^T = K Q^T and dP^T = V dO^T: one query per lane, so LSE and delta are
+// per-lane scalars) and its dQ^T accumulator in registers; K/V tiles of 64 keys are
+// double-buffered in LDS the same way; K^T comes from the transposing read.
+//
+// Eight waves, two per SIMD, keep each wave within 256 registers, so that one wave's
+// matrix instructions run while the other does its exponentials and conversions (a wave
+// does not overlap the two itself).
 //
 // Both run in ONE launch: the grid is grouped per (batch|sequence, head), each group
 // holding that head's dK/dV workgroups followed by its dQ workgroups, and groups
 // are dealt to XCDs in contiguous ranges.  Every XCD therefore gets the same mix
 // of the two workgroup kinds, and the two kinds of one head share its Q/K/V/dO
 // in that XCD's L2.
-//
-// dQ kernel: one workgroup = 4 waves = 128 query rows; each wave keeps Q and
-// dO rows (B operands of S^T = K Q^T and dP^T = V dO^T: one query per lane, so
-// LSE and delta are per-lane scalars) and its dQ^T accumulator in registers;
-// K/V tiles of 64 keys are double-buffered in LDS the same way; K^T comes from
-// the transposing read.
 //
 // Partial tiles (a ragged tail, a mask edge) zero the excluded weights in a
 // branch taken only there, so full tiles carry no per-element mask work.
@@ -111,19 +114,35 @@ __device__ __forceinline__ Slice decode(const BwdParams& p, int group, int tile)
   return s;
 }
 
-__device__ __forceinline__ float pick16(const f32x4& a, const f32x4& b, const f32x4& c,
-                                        const f32x4& d, int r) {
-  return r < 4 ? a[r & 3] : r < 8 ? b[r & 3] : r < 12 ? c[r & 3] : d[r & 3];
+// The 16 per-row values of a score register tile, from LDS: register r's row value sits at
+// p[16 * (r / 8) + r % 8].
+__device__ __forceinline__ f32x16 row_values16(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(p + 16), d = *reinterpret_cast<const f32x4*>(p + 20);
+  f32x16 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+    v[8 + i] = c[i];
+    v[12 + i] = d[i];
+  }
+  return v;
 }
 
 // ------------------------------------------------------------------ dK / dV
 
 template <int D>
 struct DkdvSmem {
-  static constexpr int BQ = 64;  // query rows per staged tile (two 32-row sub-tiles)
-  char q[2][BQ * 2 * D];
+  static constexpr int BN = 128;  // keys per workgroup: 4 blocks of 32
+  static constexpr int BQ = 64;   // query rows per staged tile: 2 sub-tiles of 32
+  // The Q/dO tiles come first: LDS reads address at most 64 KB past a register, so with
+  // all four of them in the first 64 KB one set of per-lane offsets serves every buffer.
+  char q[2][BQ * 2 * D];          // double-buffered Q and dO tiles
   char o[2][BQ * 2 * D];
-  float l[2][BQ];
+  char k[BN * 2 * D];             // K and V of the workgroup's keys, loaded once
+  char v[BN * 2 * D];
+  float l[2][BQ];                 // LSE * log2(e) and delta of the tile's rows
   float d[2][BQ];
 };
 
@@ -148,59 +167,74 @@ __device__ __forceinline__ void perm_tr_offsets(int lane, int (&off)[D / 32][2])
                                      32 * mb + 16 * (g & 1) + 4 * (src & 3));
 }
 
+// dK/dV: 8 waves, 128 keys.  Wave w owns key block w%4 (32 keys, one per lane) and
+// query sub-tile w/4 of every 64-row tile, so two waves accumulate partial dK/dV for
+// the same keys; they are summed through LDS at the end.  K and V stay in LDS (not in
+// registers), which keeps a wave within 256 registers: two waves per SIMD, so one
+// wave's MFMAs run while the other does its softmax VALU work.
 template <int D, bool VARLEN>
 __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, DkdvSmem<D>& sm) {
-  constexpr int BN = 128, BQ = DkdvSmem<D>::BQ;
+  constexpr int BN = DkdvSmem<D>::BN, BQ = DkdvSmem<D>::BQ, NW = 8;
   constexpr int RB = 2 * D;
   constexpr int NKS = D / 16, NMB = D / 32;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int hl = lane >> 5, l32 = lane & 31;
+  const int kblk = wave & 3, sub = wave >> 2;
   const int kb0 = sl.tile * BN;
   if (kb0 >= sl.nk) return;  // block-uniform
   const long rs = (long)p.H * D;
   const int nq = sl.nq, nk = sl.nk;
 
-  const int key = kb0 + wave * 32 + l32;
+  const int key = kb0 + 32 * kblk + l32;
   bool kvalid = key < nk;
   if (kvalid && sl.mask) kvalid = sl.mask[key] != 0;
   const uint64_t kball = __ballot(kvalid);
-
-  // This lane's key row: B operand of S = Q K^T and dP = dO V^T.
-  bf16x8 kreg[NKS], vreg[NKS];
-  {
-    const long off = ((long)sl.krow0 + min(key, nk - 1)) * rs + (long)sl.head * D + 8 * hl;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kreg[ks] = as_bf16x8(ld16(p.k + off + 16 * ks));
-      vreg[ks] = as_bf16x8(ld16(p.v + off + 16 * ks));
-    }
-  }
 
   int qoff[NKS], troff[NMB][2];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qoff[ks] = tile_off<D>(l32, 2 * ks + hl);
   perm_tr_offsets<D>(lane, troff);
 
+  auto same_row = [](int r) { return r; };
+  auto qrow_of = [](int r) { return perm32_row(r); };
+  const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
+  const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
   const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.head * D;
   const bf16* obase = p.dout + (long)sl.qrow0 * rs + (long)sl.head * D;
-  auto qrow_of = [](int r) { return perm32_row(r); };
-  TileLoader<D, BQ, 4> ld;
+  {
+    TileLoader<D, BN, NW> kvld;
+    kvld.init(rs, same_row);
+    kvld.issue(sm.k, kbase, rs, kb0, nk, same_row);
+    kvld.issue(sm.v, vbase, rs, kb0, nk, same_row);
+  }
+  TileLoader<D, BQ, 4> ld;  // used by waves 0..3
   ld.init(rs, qrow_of);
-  float lr = 0.f, dl = 0.f;
+  // LSE and delta of the next tile are loaded raw (row clamped, no arithmetic) ahead of
+  // its asynchronous copy and only used when published after the current tile's
+  // compute: a use right after the load would make the wave wait for the whole copy.
+  float lraw = 0.f, draw = 0.f;
   auto issue = [&](int q0, char* qt, char* ot) {
-    ld.issue(qt, qbase, rs, q0, nq, qrow_of);
-    ld.issue(ot, obase, rs, q0, nq, qrow_of);
-    if (tid < BQ) {
-      const int qi = q0 + tid;
-      lr = qi < nq ? p.lse[sl.lse_base + qi] * kLog2e : INFINITY;
-      dl = qi < nq ? p.delta[sl.lse_base + qi] : 0.f;
+    const long qi = sl.lse_base + min(q0 + lane, nq - 1);
+    lraw = p.lse[qi];
+    draw = p.delta[qi];
+    // Only the sub-tile-0 waves copy: right after the barrier the copies queue up in the
+    // memory pipeline and stall the waves that issue them (32 KB at ~64 B/clock), and
+    // meanwhile the sub-tile-1 wave of each SIMD has its matrix unit to itself.
+    if (sub == 0) {
+      ld.issue(qt, qbase, rs, q0, nq, qrow_of);
+      ld.issue(ot, obase, rs, q0, nq, qrow_of);
     }
   };
-  auto publish_stats = [&](float* lt, float* dt) {
+  // Published per row: -LSE/scale and -delta, the starting values of the S and dP
+  // accumulators (rows past the end get -inf, so their P is 0).
+  const float nis = -1.f / p.scale;
+  auto publish_stats = [&](int q0, float* lt, float* dt) {
     if (tid < BQ) {
-      lt[tid] = lr;
-      dt[tid] = dl;
+      const bool in = q0 + tid < nq;
+      lt[tid] = in ? lraw * nis : -INFINITY;
+      dt[tid] = in ? -draw : 0.f;
     }
   };
 
@@ -208,93 +242,83 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
   const float c2 = p.c2;
+  const int qr = sub * 32 * RB, kr = kblk * 32 * RB;
 
-  // Three phases per 32-query sub-tile: scores A (S, dP MFMAs), weights B (VALU: P,
-  // dS), gradients C (dV, dK MFMAs).  They are issued as A0 | A1 B0 | C0 B1 | C1, with
-  // hard scheduling boundaries between the groups, so that each VALU phase sits in
-  // one scheduling region with independent MFMAs.  No masking is needed here: with
-  // one key per lane, P and dS of an excluded key only reach that key's own dK/dV
-  // accumulators, which are written as zeros at the end.
-  auto scores = [&](const char* qt, const char* ot, int sub, f32x16& s, f32x16& dp) {
-    const int rb = sub * 32 * RB;
-    s = f32x16{};
-    dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) s = mfma32(lds_row16(qt, rb + qoff[ks]), kreg[ks], s);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) dp = mfma32(lds_row16(ot, rb + qoff[ks]), vreg[ks], dp);
-  };
-  auto weights = [&](const float* lt, const float* dt, int sub, f32x16& s, f32x16& dp,
-                     bf16x8 (&pk)[2], bf16x8 (&ds)[2]) {
+  // One 32x32 (query x key) step: scores S = Q K^T and dP = dO V^T (one key per lane),
+  // weights P = exp(scale S - LSE) and dS = P (dP - delta), then dV^T += dO^T P and
+  // dK^T += Q^T dS.  The S and dP accumulators start from their rows' -LSE/scale and
+  // -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in registers.
+  // No masking here: with one key per lane, P and dS of an excluded key only reach that
+  // key's own accumulators, which are stored as zeros.
+  auto compute = [&](const char* kt, const char* vt, const char* qt, const char* ot,
+                     const float* lt, const float* dt) {
     // Register r holds query 32*sub + 16*(r/8) + 8*hl + r%8 of the tile.
-    const float* Lp = lt + 32 * sub + 8 * hl;
-    const float* Dp = dt + 32 * sub + 8 * hl;
-    const f32x4 L0 = *reinterpret_cast<const f32x4*>(Lp), L1 = *reinterpret_cast<const f32x4*>(Lp + 4);
-    const f32x4 L2 = *reinterpret_cast<const f32x4*>(Lp + 16), L3 = *reinterpret_cast<const f32x4*>(Lp + 20);
-    const f32x4 D0 = *reinterpret_cast<const f32x4*>(Dp), D1 = *reinterpret_cast<const f32x4*>(Dp + 4);
-    const f32x4 D2 = *reinterpret_cast<const f32x4*>(Dp + 16), D3 = *reinterpret_cast<const f32x4*>(Dp + 20);
+    f32x16 s = row_values16(lt + 32 * sub + 8 * hl), dp = row_values16(dt + 32 * sub + 8 * hl);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      s = mfma32(lds_row16(qt, qr + qoff[ks]), lds_row16(kt, kr + qoff[ks]), s);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      dp = mfma32(lds_row16(ot, qr + qoff[ks]), lds_row16(vt, kr + qoff[ks]), dp);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -pick16(L0, L1, L2, L3, r)));
-      dp[r] = s[r] * (dp[r] - pick16(D0, D1, D2, D3, r));
+      s[r] = __builtin_amdgcn_exp2f(s[r] * c2);
+      dp[r] = s[r] * dp[r];
     }
-    pk[0] = pack8(s, 0);
-    pk[1] = pack8(s, 8);
-    ds[0] = pack8(dp, 0);
-    ds[1] = pack8(dp, 8);
-  };
-  auto grads = [&](const char* qt, const char* ot, int sub, const bf16x8 (&pk)[2], const bf16x8 (&ds)[2]) {
-    const int rb = sub * 32 * RB;
+    const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
+    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-      dvacc[mb] = mfma32(lds_tr8(ot + rb, troff[mb][0], troff[mb][1]), pk[0], dvacc[mb]);
-      dvacc[mb] = mfma32(lds_tr8(ot + rb + 16 * RB, troff[mb][0], troff[mb][1]), pk[1], dvacc[mb]);
-      dkacc[mb] = mfma32(lds_tr8(qt + rb, troff[mb][0], troff[mb][1]), ds[0], dkacc[mb]);
-      dkacc[mb] = mfma32(lds_tr8(qt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds[1], dkacc[mb]);
+      dvacc[mb] = mfma32(lds_tr8(ot + qr, troff[mb][0], troff[mb][1]), pk0, dvacc[mb]);
+      dvacc[mb] = mfma32(lds_tr8(ot + qr + 16 * RB, troff[mb][0], troff[mb][1]), pk1, dvacc[mb]);
+      dkacc[mb] = mfma32(lds_tr8(qt + qr, troff[mb][0], troff[mb][1]), ds0, dkacc[mb]);
+      dkacc[mb] = mfma32(lds_tr8(qt + qr + 16 * RB, troff[mb][0], troff[mb][1]), ds1, dkacc[mb]);
     }
-  };
-  static_assert(BQ == 64, "the phase order below assumes two sub-tiles");
-  auto compute = [&](const char* qt, const char* ot, const float* lt, const float* dt) {
-    f32x16 s0, dp0, s1, dp1;
-    bf16x8 pk0[2], ds0[2], pk1[2], ds1[2];
-    // Scheduling regions: A0 | A1 B0 | C0 B1 | C1 (each pair is independent work).
-    scores(qt, ot, 0, s0, dp0);
-    __builtin_amdgcn_sched_barrier(0);
-    scores(qt, ot, 1, s1, dp1);
-    weights(lt, dt, 0, s0, dp0, pk0, ds0);
-    __builtin_amdgcn_sched_barrier(0);
-    grads(qt, ot, 0, pk0, ds0);
-    weights(lt, dt, 1, s1, dp1, pk1, ds1);
-    __builtin_amdgcn_sched_barrier(0);
-    grads(qt, ot, 1, pk1, ds1);
   };
 
   const int ntiles = (nq + BQ - 1) / BQ;
-  // The current and the next tile's buffers are distinct __restrict__ parameters, so
-  // once inlined the compiler can tell reads of one from the asynchronous copy into
-  // the other (without that it waits for the copy before the first LDS read).
-  auto step = [&](int j, const char* __restrict__ cq, const char* __restrict__ co,
+  // All tile buffers are distinct __restrict__ parameters, so once inlined the compiler
+  // can tell reads of the current tile from the asynchronous copy into the next one
+  // (without that it waits for the copy before the first LDS read).
+  auto step = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt,
+                  const char* __restrict__ cq, const char* __restrict__ co,
                   const float* __restrict__ cl, const float* __restrict__ cd, char* __restrict__ nq_,
                   char* __restrict__ no_, float* __restrict__ nl, float* __restrict__ nd) {
     const bool more = j + 1 < ntiles;
-    if (more) issue((j + 1) * BQ, nq_, no_);
-    if (kball != 0) compute(cq, co, cl, cd);
-    if (more) publish_stats(nl, nd);
+    const int q1 = (j + 1) * BQ;
+    if (more) issue(q1, nq_, no_);
+    if (kball != 0) compute(kt, vt, cq, co, cl, cd);
+    if (more) publish_stats(q1, nl, nd);
     wait_tile_loads();
     __syncthreads();
   };
   if (ntiles > 0) {
     issue(0, sm.q[0], sm.o[0]);
-    publish_stats(sm.l[0], sm.d[0]);
-    wait_tile_loads();
+    publish_stats(0, sm.l[0], sm.d[0]);
   }
+  wait_tile_loads();
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, sm.q[0], sm.o[0], sm.l[0], sm.d[0], sm.q[1], sm.o[1], sm.l[1], sm.d[1]);
-    if (j + 1 < ntiles) step(j + 1, sm.q[1], sm.o[1], sm.l[1], sm.d[1], sm.q[0], sm.o[0], sm.l[0], sm.d[0]);
+    step(j, sm.k, sm.v, sm.q[0], sm.o[0], sm.l[0], sm.d[0], sm.q[1], sm.o[1], sm.l[1], sm.d[1]);
+    if (j + 1 < ntiles)
+      step(j + 1, sm.k, sm.v, sm.q[1], sm.o[1], sm.l[1], sm.d[1], sm.q[0], sm.o[0], sm.l[0], sm.d[0]);
   }
 
-  if (key < nk) {
+  // Sum the two query halves: waves of sub-tile 1 park their accumulators in LDS (the
+  // tile buffers are free now), waves of sub-tile 0 add them and store.
+  static_assert(2 * 4 * NMB * 16 * 64 * sizeof(float) <= sizeof(DkdvSmem<D>), "reduction space");
+  float* red = reinterpret_cast<float*>(&sm);
+  if (sub == 1) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[((kblk * NMB + mb) * 16 + r) * 64 + lane] = dkacc[mb][r];
+        red[(((4 + kblk) * NMB + mb) * 16 + r) * 64 + lane] = dvacc[mb][r];
+      }
+  }
+  __syncthreads();
+  if (sub == 0 && key < nk) {
     const long off = ((long)sl.krow0 + key) * rs + (long)sl.head * D + 4 * hl;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -303,8 +327,11 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
         bf16x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = (bf16)(kvalid ? dkacc[mb][4 * j4 + e] * p.scale : 0.f);
-          b[e] = (bf16)(kvalid ? dvacc[mb][4 * j4 + e] : 0.f);
+          const int r = 4 * j4 + e;
+          const float dkv = dkacc[mb][r] + red[((kblk * NMB + mb) * 16 + r) * 64 + lane];
+          const float dvv = dvacc[mb][r] + red[(((4 + kblk) * NMB + mb) * 16 + r) * 64 + lane];
+          a[e] = (bf16)(kvalid ? dkv * p.scale : 0.f);
+          b[e] = (bf16)(kvalid ? dvv : 0.f);
         }
         *reinterpret_cast<bf16x4*>(p.dk + off + 32 * mb + 8 * j4) = a;
         *reinterpret_cast<bf16x4*>(p.dv + off + 32 * mb + 8 * j4) = b;
@@ -316,11 +343,12 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 
 template <int D, bool VARLEN>
 __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqSmem<D>& sm) {
-  constexpr int BM = 128, BN = DqSmem<D>::BN;
+  constexpr int BM = 256, BN = DqSmem<D>::BN, NW = 8;
   constexpr int RB = 2 * D;
   constexpr int NKS = D / 16, NMB = D / 32;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int hl = lane >> 5, l32 = lane & 31;
   const int qb = sl.tile * BM;
   if (qb >= sl.nq) return;  // block-uniform
@@ -348,17 +376,15 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
   auto krow_of = [](int r) { return perm32_row(r); };
-  TileLoader<D, BN, 4> ld;
+  TileLoader<D, BN, 4> ld;  // used by waves 0..3
   ld.init(rs, krow_of);
+  // Only waves 0..3 copy (see dkdv_block): while they stall at issue, waves 4..7, one per
+  // SIMD, keep the matrix units busy.
   auto issue = [&](int k0, char* kt, char* vt) {
-    ld.issue(kt, kbase, rs, k0, nk, krow_of);
-    ld.issue(vt, vbase, rs, k0, nk, krow_of);
-  };
-  auto tile_valid = [&](int k0) -> uint64_t {
-    const int kk = k0 + lane;
-    bool ok = kk < nk;
-    if (ok && sl.mask) ok = sl.mask[kk] != 0;
-    return __ballot(ok);
+    if (wave < 4) {
+      ld.issue(kt, kbase, rs, k0, nk, krow_of);
+      ld.issue(vt, vbase, rs, k0, nk, krow_of);
+    }
   };
 
   f32x16 dqacc[NMB];
@@ -425,14 +451,17 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 
   const int ntiles = (nk + BN - 1) / BN;
   uint64_t vw = 0;
+  const KeyValidity kv{sl.mask, nk};
+  uint32_t mbytes = 0;  // raw mask bytes of tile j + 1 during step j
   // Current and next tile buffers as distinct __restrict__ parameters (see dkdv_block).
   auto step = [&](int j, const char* __restrict__ ck, const char* __restrict__ cv,
                   char* __restrict__ nk_, char* __restrict__ nv) {
     const bool more = j + 1 < ntiles;
     uint64_t vw_next = 0;
     if (more) {
+      vw_next = kv.word((j + 1) * BN, mbytes);
+      mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
       issue((j + 1) * BN, nk_, nv);
-      vw_next = tile_valid((j + 1) * BN);
     }
     if (vw != 0) compute(ck, cv, vw);
     wait_tile_loads();
@@ -440,8 +469,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     vw = vw_next;
   };
   if (ntiles > 0) {
+    vw = kv.word(0, kv.load(0));
+    mbytes = kv.load(BN);
     issue(0, sm.k[0], sm.v[0]);
-    vw = tile_valid(0);
     wait_tile_loads();
   }
   __syncthreads();
@@ -467,7 +497,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 // One launch for the whole backward.  Logical workgroup ids are grouped per
 // (outer, head): [dK/dV tiles of that head][dQ tiles of that head].
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   union Smem {
     DkdvSmem<D> kv;
     DqSmem<D> q;
@@ -487,7 +517,7 @@ static hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
   if (p.n_blocks == 0) return hipSuccess;
   void* args[] = {const_cast<BwdParams*>(&p)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kernel<D, VARLEN>), dim3(p.n_blocks),
-                         dim3(256), args, 0, stream);
+                         dim3(512), args, 0, stream);
 }
 
 hipError_t launch_bwd(int D, bool varlen, const BwdParams& p, hipStream_t stream) {

@@ -107,12 +107,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     kld.issue(kt, kbase, rs, k0, nk, krow);
     vld.issue(vt, vbase, rs, k0, nk, vrow);
   };
-  auto tile_valid = [&](int k0) -> uint64_t {
-    const int key = k0 + lane;
-    bool ok = key < nk;
-    if (ok && mask) ok = mask[key] != 0;
-    return __ballot(ok);
-  };
 
   f32x16 oacc[NMB];
 #pragma unroll
@@ -184,6 +178,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   const int ntiles = (nk + BN - 1) / BN;
   uint64_t vw = 0;
+  const KeyValidity kv{mask, nk};
+  uint32_t mbytes = 0;  // raw mask bytes of tile j + 1 during step j
   // Current and next tile buffers as distinct __restrict__ parameters: once inlined,
   // the compiler can tell reads of one from the asynchronous copy into the other
   // (without that it waits for the copy before the first LDS read).
@@ -192,8 +188,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const bool more = j + 1 < ntiles;
     uint64_t vw_next = 0;
     if (more) {
+      vw_next = kv.word((j + 1) * BN, mbytes);
+      mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
       issue((j + 1) * BN, kn, vn);
-      vw_next = tile_valid((j + 1) * BN);
     }
     if (vw != 0) compute(kt, vt, vw);
     wait_tile_loads();
@@ -201,8 +198,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     vw = vw_next;
   };
   if (ntiles > 0) {
+    vw = kv.word(0, kv.load(0));
+    mbytes = kv.load(BN);
     issue(0, sK0, sV0);
-    vw = tile_valid(0);
     wait_tile_loads();
   }
   __syncthreads();

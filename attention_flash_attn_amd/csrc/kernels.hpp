@@ -42,7 +42,7 @@ struct BwdParams {
 };
 
 constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
-constexpr int kDqBlockM = 128;    // query rows per dQ workgroup
+constexpr int kDqBlockM = 256;    // query rows per dQ workgroup
 constexpr int kDkvBlockN = 128;   // key rows per dK/dV workgroup
 
 hipError_t launch_fwd(int D, bool varlen, const FwdParams& p, hipStream_t stream);

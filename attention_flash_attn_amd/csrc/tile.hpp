@@ -102,6 +102,23 @@ struct TileLoader {
 
 __device__ __forceinline__ int perm32_row(int r) { return (r & ~31) | kRowPerm(r & 31); }
 
+// Key validity of the tiles of a loop over keys: bit i of a tile's word says that key
+// k0 + i exists and is not excluded by the mask.  The mask bytes are read raw (index
+// clamped, no arithmetic) one step before they are turned into a word, so the load never
+// holds up the wave: a use right after it would wait for the tile copies issued with it.
+struct KeyValidity {
+  const uint8_t* mask;  // null: every existing key is valid
+  int nk;
+  __device__ __forceinline__ uint32_t load(int k0) const {
+    uint32_t b = 1u;
+    if (mask) b = mask[min(k0 + (int)(threadIdx.x & 63), nk - 1)];
+    return b;
+  }
+  __device__ __forceinline__ uint64_t word(int k0, uint32_t b) const {
+    return __ballot(k0 + (int)(threadIdx.x & 63) < nk && b != 0u);
+  }
+};
+
 // Wait until this wave's asynchronous tile copies have landed.
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

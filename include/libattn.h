@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* a size is negative, or scale is not finite and > 0 */
+  ATTN_ERR_SHAPE = 2,       /* a size is negative, or scale is not finite and >= 2^-64 */
   ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, or a size beyond the index range */
   ATTN_ERR_SEQLENS = 4,     /* cu_seqlens is not 0 = c0 <= c1 <= ... <= c_nseq = T */
   ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
@@ -69,7 +69,8 @@ int attn_abi_version(void);
 
 /*
  * Forward: q (B,Sq,H,D), k and v (B,Sk,H,D) bf16 -> out (B,Sq,H,D) bf16 and
- * lse (B,H,Sq) fp32.  scale multiplies q.k (callers normally pass 1/sqrt(D)).
+ * lse (B,H,Sq) fp32.  scale multiplies q.k: finite and at least 2^-64 (callers
+ * normally pass 1/sqrt(D)).
  * key_mask may be NULL.
  */
 int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,

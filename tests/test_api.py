@@ -60,6 +60,7 @@ def test_fwd_validation(L):
     assert fwd(L, scale=0.0) == SHAPE
     assert fwd(L, scale=float("nan")) == SHAPE
     assert fwd(L, scale=float("inf")) == SHAPE
+    assert fwd(L, scale=1e-30) == SHAPE  # below 2^-64
     for D in (0, 32, 96, 256):
         assert fwd(L, D=D) == UNSUP
     assert fwd(L, B=2, Sq=2 ** 30 + 1) == UNSUP
