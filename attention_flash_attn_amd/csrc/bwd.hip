@@ -32,7 +32,7 @@
 // does not overlap the two itself).
 //
 // Both run in ONE launch: the grid is grouped per (batch|sequence, head), each group
-// holding that head's dK/dV workgroups followed by its dQ workgroups, and groups
+// holding that head's dQ workgroups followed by its dK/dV workgroups, and groups
 // are dealt to XCDs in contiguous ranges.  Every XCD therefore gets the same mix
 // of the two workgroup kinds, and the two kinds of one head share its Q/K/V/dO
 // in that XCD's L2.
@@ -495,7 +495,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 }
 
 // One launch for the whole backward.  Logical workgroup ids are grouped per
-// (outer, head): [dK/dV tiles of that head][dQ tiles of that head].
+// (outer, head): [dQ tiles of that head][dK/dV tiles of that head].
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   union Smem {
@@ -506,10 +506,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   const int logical = xcd_remap(blockIdx.x, p.n_blocks);
   const int per_group = p.n_kv_tiles + p.n_q_tiles;
   const int group = logical / per_group, within = logical % per_group;
-  if (within < p.n_kv_tiles)
-    dkdv_block<D, VARLEN>(p, decode<VARLEN>(p, group, within), sm.kv);
+  // dQ workgroups (the longer ones) first, so the grid's tail holds the shorter dK/dV ones.
+  if (within >= p.n_q_tiles)
+    dkdv_block<D, VARLEN>(p, decode<VARLEN>(p, group, within - p.n_q_tiles), sm.kv);
   else
-    dq_block<D, VARLEN>(p, decode<VARLEN>(p, group, within - p.n_kv_tiles), sm.q);
+    dq_block<D, VARLEN>(p, decode<VARLEN>(p, group, within), sm.q);
 }
 
 template <int D, bool VARLEN>

@@ -14,6 +14,8 @@ uses its own algorithmic FLOPs and that duration.  The fp64 CPU oracle is
 timed beside it on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+(defaults: 10 warm-up and 50 timed steps; per-step median, min and mean are reported
+beside the mean-based value)
 """
 from __future__ import annotations
 
@@ -34,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan_shard",
                     help="wan_shard (the metric's workload) or another named workload: "
                          "probe_hs16, dit_s1024, mask_s4096, varlen4")
@@ -87,27 +89,53 @@ def describe(w):
     return f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}, BSHD bf16, non-causal, {m}"
 
 
-def cpu_baseline(w, t, rows):
-    """fp64 oracle on one head, the first `rows` query rows against all keys: forward,
-    delta, dQ of those rows and their full dK/dV contribution (same per-row work as
-    the full problem)."""
-    import numpy as np
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def oracle_head_tflops(t, b, h, rows, D):
+    """fp64 oracle on head (b, h): the first `rows` query rows against all keys, forward,
+    delta, dQ of those rows and their full dK/dV contribution (same per-row work as the
+    full problem).  Returns (TFLOP/s at the algorithmic count, seconds)."""
     import oracle
     from attention_flash_attn_amd import inputs as I
 
-    h = 0
-    q, k, v, do = (I.f64_from_bf16_bits(x[:1, :, h:h + 1]) for x in (t.q, t.k, t.v, t.do))
+    q, k, v, do = (I.f64_from_bf16_bits(x[b:b + 1, :, h:h + 1]) for x in (t.q, t.k, t.v, t.do))
     q, do = q[:, :rows], do[:, :rows]
     t0 = time.perf_counter()
     out, lse = oracle.attn_fwd(q, k, v)
     oracle.attn_bwd(q, k, v, out, lse, do)
     dt = time.perf_counter() - t0
-    flops = 3.5 * 4.0 * rows * k.shape[1] * w.D
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"one head (b=0,h=0), {rows} of {w.S} query rows x all {k.shape[1]} keys, "
-                      f"fwd+delta+dQ+dK/dV in fp64, {dt:.1f} s"}
+    return 3.5 * 4.0 * rows * k.shape[1] * D / dt / 1e12, dt
+
+
+def cpu_baseline(w, t, rows):
+    """The oracle on all host threads over one head of the workload, plus a one-thread
+    run over one head of the 1024-token DiT workload for a per-core figure."""
+    import oracle
+    from attention_flash_attn_amd import inputs as I
+
+    cores = oracle.num_threads()
+    value, dt = oracle_head_tflops(t, 0, 0, rows, w.D)
+    small = I.WORKLOADS["dit_s1024"]
+    oracle.set_num_threads(1)
+    try:
+        v1, dt1 = oracle_head_tflops(I.draw_workload(small), 0, 0, small.S, small.D)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one head (b=0,h=0), {rows} of {w.S} query rows x all {w.S} keys, "
+                      f"fwd+delta+dQ+dK/dV in fp64, {dt:.1f} s on {cores} threads of {cpu_model()}",
+            "per_core": {"value": v1, "unit": "TFLOP/s", "cores": 1,
+                         "sample": f"one head of dit_s1024 (S={small.S}, D={small.D}), same passes, "
+                                   f"{dt1:.2f} s on 1 thread"}}
 
 
 def main():
@@ -177,6 +205,7 @@ def main():
     wall = time.perf_counter() - t0
     per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                     for e in evs])  # ms
+    steps_each = np.array([e[0].elapsed_time(e[3]) for e in evs])
     step_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / K
     fwd_ms, pre_ms, bwd_ms = (float(x) for x in per.mean(0))
 
@@ -209,6 +238,12 @@ def main():
         "fwd_tflops": round(f_fwd / (fwd_ms / 1e3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / (bwd_ms / 1e3) / 1e12, 2),
         "wall_ms_per_step": round(1e3 * wall / K, 4),
+        "step_ms_stats": {"median": round(float(np.median(steps_each)), 4),
+                          "min": round(float(steps_each.min()), 4),
+                          "mean": round(float(steps_each.mean()), 4)},
+        "kernels_ms_median": {"attn_fwd": round(float(np.median(per[:, 0])), 4),
+                              "attn_bwd_preprocess": round(float(np.median(per[:, 1])), 4),
+                              "attn_bwd": round(float(np.median(per[:, 2])), 4)},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

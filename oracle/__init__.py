@@ -35,11 +35,12 @@ def _load():
     lib.oracle_attn_delta.argtypes = [i, i, i, i, _dp, _dp, _dp]
     lib.oracle_attn_bwd.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp, _dp, _dp,
                                     _dp, _dp, _dp]
+    lib.oracle_set_num_threads.argtypes = [i]
     lib.oracle_attn_varlen_fwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp]
     lib.oracle_attn_varlen_bwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                            _dp, _dp, _dp]
     for f in ("oracle_attn_fwd", "oracle_attn_delta", "oracle_attn_bwd", "oracle_attn_varlen_fwd",
-              "oracle_attn_varlen_bwd", "oracle_num_threads"):
+              "oracle_attn_varlen_bwd", "oracle_num_threads", "oracle_set_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -47,6 +48,11 @@ def _load():
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> int:
+    """Threads for the following calls (OpenMP); returns the count now in effect."""
+    return _load().oracle_set_num_threads(int(n))
 
 
 def _f64(a):

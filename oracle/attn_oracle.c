@@ -131,6 +131,12 @@ static int check_dims(int B, int Sq, int Sk, int H, int D) {
 
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads used by the parallel loops from now on (n >= 1); returns the new count. */
+int oracle_set_num_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+}
+
 /* ---------------------------------------------------------------- dense BSHD */
 
 int oracle_attn_fwd(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
