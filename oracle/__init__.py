@@ -36,11 +36,14 @@ def _load():
     lib.oracle_attn_bwd.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp, _dp, _dp,
                                     _dp, _dp, _dp]
     lib.oracle_set_num_threads.argtypes = [i]
+    lib.oracle_attn_lse_merge.argtypes = [i, i, i, i, i, ctypes.POINTER(_dp), ctypes.POINTER(_dp),
+                                          _dp, _dp]
     lib.oracle_attn_varlen_fwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp]
     lib.oracle_attn_varlen_bwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                            _dp, _dp, _dp]
     for f in ("oracle_attn_fwd", "oracle_attn_delta", "oracle_attn_bwd", "oracle_attn_varlen_fwd",
-              "oracle_attn_varlen_bwd", "oracle_num_threads", "oracle_set_num_threads"):
+              "oracle_attn_varlen_bwd", "oracle_num_threads", "oracle_set_num_threads",
+              "oracle_attn_lse_merge"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -150,3 +153,21 @@ def attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None):
                                           _p(q), _p(k), _p(v), _p(out), _p(lse), _p(dout),
                                           _p(delta), _p(dq), _p(dk), _p(dv)))
     return delta, dq, dk, dv
+
+
+def attn_lse_merge(outs, lses):
+    """Merge partial results of disjoint key chunks: outs[c] (B,S,H,D), lses[c] (B,H,S)
+    -> (out, lse) of attention over all the chunks' keys."""
+    outs = [_f64(o) for o in outs]
+    lses = [_f64(l) for l in lses]
+    n = len(outs)
+    assert n >= 1 and len(lses) == n
+    B, S, H, D = outs[0].shape
+    for o, l in zip(outs, lses):
+        assert o.shape == (B, S, H, D) and l.shape == (B, H, S)
+    out = np.empty_like(outs[0])
+    lse = np.empty_like(lses[0])
+    op = (_dp * n)(*[_p(o) for o in outs])
+    lp = (_dp * n)(*[_p(l) for l in lses])
+    _check(_load().oracle_attn_lse_merge(n, B, S, H, D, op, lp, _p(out), _p(lse)))
+    return out, lse

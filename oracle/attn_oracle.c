@@ -287,3 +287,46 @@ int oracle_attn_varlen_bwd(int nseq, const int32_t* cu, int H, int D, double sca
   if (!delta_out) free(delta);
   return 0;
 }
+
+/* ---------------------------------------------------------------- chunk merge */
+
+/*
+ * Merge of partial results over disjoint key chunks (ring / context-parallel
+ * attention, whose backward diffusers PR #14834 names as missing in its
+ * description).  It follows from the definition at the top of this file: with the
+ * keys split into chunks c and lse_c, out_c each chunk's own forward,
+ *   LSE_i = log sum_c sum_{j in c} exp(s_ij) = log sum_c exp(lse_c,i)
+ *   out_i = sum_c sum_{j in c} exp(s_ij - LSE_i) v_j = sum_c exp(lse_c,i - LSE_i) out_c,i.
+ * Computed as written; the largest lse_c,i is factored out of the first sum only to keep
+ * exp() in range.  A row with lse_c,i = -inf in every chunk gets out = 0, LSE = -inf.
+ * outs[c] are (B, S, H, D), lses[c] (B, H, S).
+ */
+int oracle_attn_lse_merge(int n, int B, int S, int H, int D, const double* const* outs,
+                          const double* const* lses, double* out, double* lse) {
+  if (n < 1 || !check_dims(B, S, S, H, D)) return 1;
+  const long rows = (long)B * S * H;
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    const long h = r % H, bs = r / H, i = bs % S, b = bs / S;
+    const long li = (b * H + h) * S + i;
+    double m = -INFINITY;
+    for (int c = 0; c < n; ++c)
+      if (lses[c][li] > m) m = lses[c][li];
+    double* o = out + r * D;
+    if (m == -INFINITY) {
+      lse[li] = -INFINITY;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      continue;
+    }
+    double sum = 0.0;
+    for (int c = 0; c < n; ++c) sum += exp(lses[c][li] - m);
+    const double L = m + log(sum);
+    lse[li] = L;
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int c = 0; c < n; ++c) acc += exp(lses[c][li] - L) * outs[c][r * D + d];
+      o[d] = acc;
+    }
+  }
+  return 0;
+}
