@@ -52,8 +52,12 @@ def lib():
     L.attn_bwd.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_varlen_fwd.argtypes = [i, vp, vp, i, i, f, vp, vp, vp, vp, vp, vp]
     L.attn_varlen_bwd.argtypes = [i, vp, vp, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_lse_merge.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp]
+    L.attn_bwd_accum.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
+    L.attn_cast_bf16.argtypes = [ctypes.c_int64, vp, vp, vp]
     for name in ("attn_abi_version", "attn_fwd", "attn_bwd_preprocess", "attn_bwd",
-                 "attn_varlen_fwd", "attn_varlen_bwd"):
+                 "attn_varlen_fwd", "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum",
+                 "attn_cast_bf16"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -259,3 +263,70 @@ def attn_varlen_bwd(q, k, v, lse, delta, dout, cu_seqlens, scale=None, dq=None, 
                                                     _ptr(delta), _ptr(o3), _ptr(dq), _ptr(dk),
                                                     _ptr(dv), _stream()))
     return dq, dk, dv
+
+
+MAX_MERGE_CHUNKS = 16
+
+
+def attn_lse_merge(outs, lses, out=None, lse=None):
+    """out, lse = attn_lse_merge([out_c], [lse_c]): merge partial results of disjoint key
+    chunks (each out_c (B,S,H,D) bf16 normalised over its chunk, lse_c (B,H,S) fp32).
+    out / lse may be one chunk's own tensors (in-place accumulation)."""
+    torch = _torch()
+    n = len(outs)
+    if n != len(lses) or not 1 <= n <= MAX_MERGE_CHUNKS:
+        raise ValueError(f"need 1..{MAX_MERGE_CHUNKS} chunks with one lse each, got {n}/{len(lses)}")
+    B, S, H, D = outs[0].shape
+    for c in range(n):
+        _want(outs[c], f"outs[{c}]", (B, S, H, D), torch.bfloat16)
+        _want(lses[c], f"lses[{c}]", (B, H, S), torch.float32)
+    out = torch.empty_like(outs[0]) if out is None else out
+    lse = torch.empty_like(lses[0]) if lse is None else lse
+    _want(out, "out", (B, S, H, D), torch.bfloat16)
+    _want(lse, "lse", (B, H, S), torch.float32)
+    optr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    lptr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in lses])
+    _check("attn_lse_merge", lib().attn_lse_merge(n, B, S, H, D, optr, lptr, _ptr(out), _ptr(lse),
+                                                  _stream()))
+    return out, lse
+
+
+ACC_DQ, ACC_DKDV = 1, 2
+
+
+def attn_bwd_accum(q, k, v, lse, delta, dout, dq_acc, dk_acc, dv_acc, key_mask=None, scale=None,
+                   add_dq=True, add_dkdv=True):
+    """One key chunk's dQ, dK, dV into fp32 buffers (q, dout of all rows with the whole key
+    set's lse and delta; k, v, key_mask of the chunk): added to the buffers' contents
+    (add_dq / add_dkdv) or written over them."""
+    torch = _torch()
+    B, Sq, Sk, H, D = _dims(q, k)
+    _want(q, "q", (B, Sq, H, D), torch.bfloat16)
+    _want(k, "k", (B, Sk, H, D), torch.bfloat16)
+    _want(v, "v", (B, Sk, H, D), torch.bfloat16)
+    _want(dout, "dout", (B, Sq, H, D), torch.bfloat16)
+    _want(lse, "lse", (B, H, Sq), torch.float32)
+    _want(delta, "delta", (B, H, Sq), torch.float32)
+    _want(dq_acc, "dq_acc", (B, Sq, H, D), torch.float32)
+    _want(dk_acc, "dk_acc", (B, Sk, H, D), torch.float32)
+    _want(dv_acc, "dv_acc", (B, Sk, H, D), torch.float32)
+    m = _mask_arg(key_mask, B, Sk, H)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check("attn_bwd_accum", lib().attn_bwd_accum(B, Sq, Sk, H, D, scale, _ptr(q), _ptr(k), _ptr(v),
+                                                  _ptr(m), _ptr(lse), _ptr(delta), _ptr(dout),
+                                                  _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc),
+                                                  (ACC_DQ if add_dq else 0) |
+                                                  (ACC_DKDV if add_dkdv else 0), _stream()))
+    return dq_acc, dk_acc, dv_acc
+
+
+def attn_cast_bf16(src, dst=None):
+    """bf16 copy (nearest even) of an fp32 tensor, e.g. an accumulated gradient."""
+    torch = _torch()
+    if not isinstance(src, torch.Tensor) or src.dtype != torch.float32:
+        raise TypeError("src must be a float32 tensor")
+    dst = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device) if dst is None else dst
+    _want(src, "src", tuple(src.shape), torch.float32)
+    _want(dst, "dst", tuple(src.shape), torch.bfloat16)
+    _check("attn_cast_bf16", lib().attn_cast_bf16(src.numel(), _ptr(src), _ptr(dst), _stream()))
+    return dst

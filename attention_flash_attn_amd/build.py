@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "merge.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

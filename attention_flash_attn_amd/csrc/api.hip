@@ -15,7 +15,7 @@ using attn::FwdParams;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
 // The backward starts its score accumulators from -LSE/scale; the lower bound keeps that
@@ -156,7 +156,66 @@ int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, co
   p.n_kv_tiles = (int)cdiv(Sk, attn::kDkvBlockN);
   p.n_q_tiles = (int)cdiv(Sq, attn::kDqBlockM);
   p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * B;
-  return status_of(attn::launch_bwd(D, false, p, s));
+  return status_of(attn::launch_bwd(D, false, false, p, s));
+}
+
+int attn_bwd_accum(int B, int Sq, int Sk, int H, int D, float scale, const void* q,
+                   const void* k, const void* v, const uint8_t* key_mask, const float* lse,
+                   const float* delta, const void* dout, float* dq_acc, float* dk_acc,
+                   float* dv_acc, int flags, void* stream) {
+  const int st = check_dense(B, Sq, Sk, H, D, scale);
+  if (st != ATTN_OK) return st;
+  if (flags & ~(ATTN_ACC_DQ | ATTN_ACC_DKDV)) return ATTN_ERR_SHAPE;
+  const bool hq = (long)B * Sq * H > 0, hk = (long)B * Sk * H > 0;
+  if (missing(q, hq) || missing(lse, hq) || missing(delta, hq) || missing(dout, hq) ||
+      missing(dq_acc, hq) || missing(k, hk) || missing(v, hk) || missing(dk_acc, hk) ||
+      missing(dv_acc, hk))
+    return ATTN_ERR_NULL;
+  if ((long)B * H == 0) return ATTN_OK;
+  BwdParams p = bwd_params(B, Sq, Sk, H, scale, q, k, v, key_mask, lse, delta, dout, nullptr,
+                           nullptr, nullptr, nullptr);
+  p.dq_acc = dq_acc;
+  p.dk_acc = dk_acc;
+  p.dv_acc = dv_acc;
+  p.acc_flags = flags;
+  p.n_kv_tiles = (int)cdiv(Sk, attn::kDkvBlockN);
+  p.n_q_tiles = (int)cdiv(Sq, attn::kDqBlockM);
+  p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * B;
+  return status_of(attn::launch_bwd(D, false, true, p, static_cast<hipStream_t>(stream)));
+}
+
+int attn_lse_merge(int n, int B, int S, int H, int D, const void* const* outs,
+                   const float* const* lses, void* out, float* lse, void* stream) {
+  if (n < 1 || B < 0 || S < 0 || H < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (!head_dim_ok(D) || n > attn::kMaxMergeChunks) return ATTN_ERR_UNSUPPORTED;
+  if (!outs || !lses) return ATTN_ERR_NULL;
+  const long rows = (long)B * S * H;
+  for (int i = 0; i < n; ++i)
+    if (missing(outs[i], rows > 0) || missing(lses[i], rows > 0)) return ATTN_ERR_NULL;
+  if (missing(out, rows > 0) || missing(lse, rows > 0)) return ATTN_ERR_NULL;
+  if (rows == 0) return ATTN_OK;
+  if (cdiv(rows, 256 / (D / 8)) > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  attn::MergeParams p{};
+  for (int i = 0; i < n; ++i) {
+    p.out[i] = static_cast<const __bf16*>(outs[i]);
+    p.lse[i] = lses[i];
+  }
+  p.dst = static_cast<__bf16*>(out);
+  p.dst_lse = lse;
+  p.rows = rows;
+  p.S = S;
+  p.H = H;
+  p.n = n;
+  return status_of(attn::launch_merge(D, p, static_cast<hipStream_t>(stream)));
+}
+
+int attn_cast_bf16(int64_t n, const float* src, void* dst, void* stream) {
+  if (n < 0) return ATTN_ERR_SHAPE;
+  if (missing(src, n > 0) || missing(dst, n > 0)) return ATTN_ERR_NULL;
+  if (n == 0) return ATTN_OK;
+  if (cdiv(n, 2048) > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  return status_of(attn::launch_cast_bf16(n, src, static_cast<__bf16*>(dst),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
@@ -207,7 +266,7 @@ int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
   p.n_kv_tiles = (int)cdiv(maxlen, attn::kDkvBlockN);
   p.n_q_tiles = (int)cdiv(maxlen, attn::kDqBlockM);
   p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * nseq;
-  return status_of(attn::launch_bwd(D, true, p, s));
+  return status_of(attn::launch_bwd(D, true, false, p, s));
 }
 
 }  // extern "C"

@@ -172,7 +172,7 @@ __device__ __forceinline__ void perm_tr_offsets(int lane, int (&off)[D / 32][2])
 // the same keys; they are summed through LDS at the end.  K and V stay in LDS (not in
 // registers), which keeps a wave within 256 registers: two waves per SIMD, so one
 // wave's MFMAs run while the other does its softmax VALU work.
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool ACC>
 __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, DkdvSmem<D>& sm) {
   constexpr int BN = DkdvSmem<D>::BN, BQ = DkdvSmem<D>::BQ, NW = 8;
   constexpr int RB = 2 * D;
@@ -324,24 +324,36 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        bf16x4 a, b;
+        f32x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j4 + e;
           const float dkv = dkacc[mb][r] + red[((kblk * NMB + mb) * 16 + r) * 64 + lane];
           const float dvv = dvacc[mb][r] + red[(((4 + kblk) * NMB + mb) * 16 + r) * 64 + lane];
-          a[e] = (bf16)(kvalid ? dkv * p.scale : 0.f);
-          b[e] = (bf16)(kvalid ? dvv : 0.f);
+          a[e] = kvalid ? dkv * p.scale : 0.f;
+          b[e] = kvalid ? dvv : 0.f;
         }
-        *reinterpret_cast<bf16x4*>(p.dk + off + 32 * mb + 8 * j4) = a;
-        *reinterpret_cast<bf16x4*>(p.dv + off + 32 * mb + 8 * j4) = b;
+        const long o = off + 32 * mb + 8 * j4;
+        if (ACC) {
+          f32x4* ka = reinterpret_cast<f32x4*>(p.dk_acc + o);
+          f32x4* va = reinterpret_cast<f32x4*>(p.dv_acc + o);
+          if (p.acc_flags & 2) {
+            a += *ka;
+            b += *va;
+          }
+          *ka = a;
+          *va = b;
+        } else {
+          *reinterpret_cast<bf16x4*>(p.dk + o) = to_bf16x4(a);
+          *reinterpret_cast<bf16x4*>(p.dv + o) = to_bf16x4(b);
+        }
       }
   }
 }
 
 // ------------------------------------------------------------------ dQ
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool ACC>
 __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqSmem<D>& sm) {
   constexpr int BM = 256, BN = DqSmem<D>::BN, NW = 8;
   constexpr int RB = 2 * D;
@@ -368,10 +380,28 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const float lse2 = qrow < nq ? p.lse[sl.lse_base + qrow] * kLog2e : INFINITY;
   const float dl = qrow < nq ? p.delta[sl.lse_base + qrow] : 0.f;
 
+  // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
+  // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
+  // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt at every step from the step-0
+  // offsets, which keeps 14 registers free for the loop.
+  int koff0 = tile_off<D>(l32, hl), tr0[2];
+  {
+    int troff[NMB][2];
+    perm_tr_offsets<D>(lane, troff);
+    tr0[0] = troff[0][0];
+    tr0[1] = troff[0][1];
+  }
   int koff[NKS], troff[NMB][2];
+  auto offsets = [&]() {
+    asm volatile("" : "+v"(koff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hl);
-  perm_tr_offsets<D>(lane, troff);
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = koff0 ^ (32 * ks);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      troff[mb][0] = tr0[0] ^ (64 * mb);
+      troff[mb][1] = tr0[1] ^ (64 * mb);
+    }
+  };
 
   const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
@@ -428,6 +458,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     }
   };
   auto compute = [&](const char* kt, const char* vt, uint64_t vw) {
+    offsets();
     f32x16 st0, dpt0, st1, dpt1;
     bf16x8 ds0[2], ds1[2];
     scores(kt, vt, 0, st0, dpt0);
@@ -481,22 +512,29 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   }
 
   if (qrow < nq) {
-    bf16* dqp = p.dq + ((long)sl.qrow0 + qrow) * rs + (long)sl.head * D + 4 * hl;
+    const long off = ((long)sl.qrow0 + qrow) * rs + (long)sl.head * D + 4 * hl;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        bf16x4 o;
+        const long o = off + 32 * mb + 8 * j4;
+        f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)(dqacc[mb][4 * j4 + e] * p.scale);
-        *reinterpret_cast<bf16x4*>(dqp + 32 * mb + 8 * j4) = o;
+        for (int e = 0; e < 4; ++e) x[e] = dqacc[mb][4 * j4 + e] * p.scale;
+        if (ACC) {
+          f32x4* a = reinterpret_cast<f32x4*>(p.dq_acc + o);
+          if (p.acc_flags & 1) x += *a;
+          *a = x;
+        } else {
+          *reinterpret_cast<bf16x4*>(p.dq + o) = to_bf16x4(x);
+        }
       }
   }
 }
 
 // One launch for the whole backward.  Logical workgroup ids are grouped per
 // (outer, head): [dQ tiles of that head][dK/dV tiles of that head].
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool ACC>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   union Smem {
     DkdvSmem<D> kv;
@@ -508,22 +546,26 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   const int group = logical / per_group, within = logical % per_group;
   // dQ workgroups (the longer ones) first, so the grid's tail holds the shorter dK/dV ones.
   if (within >= p.n_q_tiles)
-    dkdv_block<D, VARLEN>(p, decode<VARLEN>(p, group, within - p.n_q_tiles), sm.kv);
+    dkdv_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, within - p.n_q_tiles), sm.kv);
   else
-    dq_block<D, VARLEN>(p, decode<VARLEN>(p, group, within), sm.q);
+    dq_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, within), sm.q);
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool ACC>
 static hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
   if (p.n_blocks == 0) return hipSuccess;
   void* args[] = {const_cast<BwdParams*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kernel<D, VARLEN>), dim3(p.n_blocks),
-                         dim3(512), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kernel<D, VARLEN, ACC>),
+                         dim3(p.n_blocks), dim3(512), args, 0, stream);
 }
 
-hipError_t launch_bwd(int D, bool varlen, const BwdParams& p, hipStream_t stream) {
-  if (D == 64) return varlen ? launch_t<64, true>(p, stream) : launch_t<64, false>(p, stream);
-  return varlen ? launch_t<128, true>(p, stream) : launch_t<128, false>(p, stream);
+hipError_t launch_bwd(int D, bool varlen, bool accum, const BwdParams& p, hipStream_t stream) {
+  if (accum) {
+    if (varlen) return hipErrorInvalidValue;  // accumulating launches are dense only
+    return D == 64 ? launch_t<64, false, true>(p, stream) : launch_t<128, false, true>(p, stream);
+  }
+  if (D == 64) return varlen ? launch_t<64, true, false>(p, stream) : launch_t<64, false, false>(p, stream);
+  return varlen ? launch_t<128, true, false>(p, stream) : launch_t<128, false, false>(p, stream);
 }
 
 }  // namespace attn

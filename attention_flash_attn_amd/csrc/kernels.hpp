@@ -32,6 +32,10 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
+  float* dq_acc;  // fp32-output launches: written instead of dq/dk/dv
+  float* dk_acc;
+  float* dv_acc;
+  int acc_flags;  // bit 0: add into dq_acc, bit 1: add into dk_acc/dv_acc (else overwrite)
   const int32_t* cu;
   int B, Sq, Sk, H;
   int n_kv_tiles;  // dK/dV workgroups per (outer, head)
@@ -46,8 +50,23 @@ constexpr int kDqBlockM = 256;    // query rows per dQ workgroup
 constexpr int kDkvBlockN = 128;   // key rows per dK/dV workgroup
 
 hipError_t launch_fwd(int D, bool varlen, const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd(int D, bool varlen, const BwdParams& p, hipStream_t stream);
+// accum: fp32 dQ/dK/dV into p.dq_acc/dk_acc/dv_acc (added or overwritten per p.acc_flags)
+// instead of bf16 dq/dk/dv (dense only)
+hipError_t launch_bwd(int D, bool varlen, bool accum, const BwdParams& p, hipStream_t stream);
 hipError_t launch_delta(int D, long rows, int S, int H, const __bf16* out, const __bf16* dout,
                         float* delta, hipStream_t stream);
+
+// Merge of partial attention results over disjoint key chunks (see merge.hip).
+constexpr int kMaxMergeChunks = 16;
+struct MergeParams {
+  const __bf16* out[kMaxMergeChunks];  // (B, S, H, D) each
+  const float* lse[kMaxMergeChunks];   // (B, H, S) each
+  __bf16* dst;
+  float* dst_lse;
+  long rows;  // B * S * H
+  int S, H, n;
+};
+hipError_t launch_merge(int D, const MergeParams& p, hipStream_t stream);
+hipError_t launch_cast_bf16(long n, const float* src, __bf16* dst, hipStream_t stream);
 
 }  // namespace attn

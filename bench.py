@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=27280,
                     help="query rows of one head in the CPU-oracle sample")
+    ap.add_argument("--ring-chunks", type=int, default=0,
+                    help="time the ring / context-parallel path instead: keys split into this "
+                         "many chunks, per-chunk forwards merged by attn_lse_merge, per-chunk "
+                         "backward with the merged statistics (attn_bwd_accum), fp32 -> bf16 casts")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling the profiler's HBM counters)")
@@ -138,6 +142,101 @@ def cpu_baseline(w, t, rows):
                                    f"{dt1:.2f} s on 1 thread"}}
 
 
+def calibration_copy(mb):
+    """One plain device copy of `mb` MiB after the timed work: a known byte count that
+    scales the profiler's HBM counters."""
+    if mb <= 0:
+        return {}
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_calibration_bytes": n}
+
+
+def run_ring(args, w, t, C):
+    """The ring / context-parallel path on one GPU: the workload's keys in C chunks."""
+    import numpy as np
+    import torch
+
+    import attention_flash_attn_amd as A
+
+    if w.varlen:
+        raise SystemExit("--ring-chunks applies to dense workloads")
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = (dev(x) for x in (t.q, t.k, t.v, t.do))
+    B, S, H, D = w.B, w.S, w.H, w.D
+    bounds = [(c * S // C, (c + 1) * S // C) for c in range(C)]
+    mask = None if t.key_mask is None else torch.from_numpy(t.key_mask).cuda()
+    ks = [k[:, a:b].contiguous() for a, b in bounds]
+    vs = [v[:, a:b].contiguous() for a, b in bounds]
+    ms = [None if mask is None else mask[:, a:b].contiguous() for a, b in bounds]
+    outs = [torch.empty_like(q) for _ in bounds]
+    lses = [torch.empty((B, H, S), dtype=torch.float32, device="cuda") for _ in bounds]
+    out, lse = torch.empty_like(q), torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq_acc = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk_acc = [torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in ks]
+    dv_acc = [torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in vs]
+    dq = torch.empty_like(q)
+    dks, dvs = [torch.empty_like(x) for x in ks], [torch.empty_like(x) for x in vs]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        for c in range(C):
+            A.attn_fwd(q, ks[c], vs[c], ms[c], None, out=outs[c], lse=lses[c])
+        rec(1)
+        A.attn_lse_merge(outs, lses, out=out, lse=lse)
+        rec(2)
+        A.attn_bwd_preprocess(out, do, delta=delta)
+        rec(3)
+        for c in range(C):
+            A.attn_bwd_accum(q, ks[c], vs[c], lse, delta, do, dq_acc, dk_acc[c], dv_acc[c], ms[c],
+                             add_dq=c > 0, add_dkdv=False)
+        rec(4)
+        A.attn_cast_bf16(dq_acc, dq)
+        for c in range(C):
+            A.attn_cast_bf16(dk_acc[c], dks[c])
+            A.attn_cast_bf16(dv_acc[c], dvs[c])
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs])
+    step_ms = float(evs[0][0].elapsed_time(evs[-1][5])) / K
+    fwd_ms, merge_ms, pre_ms, bwd_ms, cast_ms = (float(x) for x in np.median(per, 0))
+    f_fwd = w.fwd_flops()
+    total = 3.5 * f_fwd
+    rows = B * S * H
+    merge_bytes = C * (rows * D * 2 + rows * 4) + rows * D * 2 + rows * 4
+    merge_gbs = merge_bytes / (merge_ms * 1e-3) / 1e9
+    return {
+        "metric": f"attention fwd+bwd TFLOP/s, ring path with the keys in {C} chunks",
+        "value": round(total / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": describe(w) + f"; keys in {C} equal chunks", "chunks": C},
+        "kernels_ms_median": {"attn_fwd x%d" % C: round(fwd_ms, 4), "attn_lse_merge": round(merge_ms, 4),
+                              "attn_bwd_preprocess": round(pre_ms, 4),
+                              "attn_bwd_accum x%d" % C: round(bwd_ms, 4),
+                              "attn_cast_bf16 x%d" % (2 * C + 1): round(cast_ms, 4)},
+        "merge_roofline": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
+                           "traffic": None, "bytes_per_launch": merge_bytes},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -155,6 +254,11 @@ def main():
     A.lib()
     w = I.WORKLOADS[args.workload]
     t = I.draw_workload(w)
+    if args.ring_chunks > 0:
+        res = run_ring(args, w, t, args.ring_chunks)
+        res.update(calibration_copy(args.copy_calibration_mb))
+        print(json.dumps(res), flush=True)
+        return
     dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = (dev(x) for x in (t.q, t.k, t.v, t.do))
     B, S, H, D = w.B, w.S, w.H, w.D
@@ -249,14 +353,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name, dom)},
     }
-    if args.copy_calibration_mb > 0:
-        n = args.copy_calibration_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = n
+    res.update(calibration_copy(args.copy_calibration_mb))
     if not args.no_cpu_baseline and not w.varlen and w.valid_lens is None:
         res["cpu_baseline"] = cpu_baseline(w, t, min(args.cpu_rows, w.S))
     print(json.dumps(res), flush=True)

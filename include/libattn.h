@@ -115,6 +115,42 @@ int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
                     const float* lse, const float* delta, const void* dout, void* dq, void* dk,
                     void* dv, void* stream);
 
+/*
+ * Merge of partial results over disjoint key chunks (ring / context-parallel attention:
+ * the Ring-Anything backward that diffusers PR #14834 names as missing (description),
+ * ring CP left unverified in diffusers PR #14341, "Not verified").  Chunk c's forward
+ * over its own keys gave outs[c] (B,S,H,D) bf16 and lses[c] (B,H,S) fp32; writes
+ *   lse = log sum_c exp(lses[c]),   out = sum_c exp(lses[c] - lse) outs[c]
+ * (fp32 inside, out rounded once to bf16).  A chunk whose lse is -inf for a row adds
+ * nothing to it; a row with -inf in every chunk gets out = 0, lse = -inf.
+ * outs and lses are HOST arrays of n DEVICE pointers, 1 <= n <= 16 (else
+ * ATTN_ERR_SHAPE / ATTN_ERR_UNSUPPORTED).  out and lse may alias one chunk's buffers
+ * (in-place accumulation); they must not partially overlap them.
+ */
+int attn_lse_merge(int n, int B, int S, int H, int D, const void* const* outs,
+                   const float* const* lses, void* out, float* lse, void* stream);
+
+/*
+ * Backward of one key chunk with the statistics of the whole key set (the merge-aware
+ * backward of ring attention, same passages as attn_lse_merge).  Arguments as attn_bwd,
+ * except that k, v, key_mask are the chunk's (Sk = chunk length), lse is the merged
+ * (whole key set) LSE and delta = rowsum(dout * merged out), and the gradients go to
+ * fp32 buffers: dq_acc (B,Sq,H,D) gets this chunk's dQ, dk_acc and dv_acc (B,Sk,H,D) the
+ * chunk's dK, dV -- added to what the buffer holds if flags has ATTN_ACC_DQ (dq_acc) /
+ * ATTN_ACC_DKDV (dk_acc, dv_acc), else written over it.  Summed over the chunks these
+ * equal the full backward (first chunk: flags 0, later chunks: ATTN_ACC_DQ); round them
+ * with attn_cast_bf16.  Other flag bits: ATTN_ERR_SHAPE.  Calls that share a buffer must
+ * be ordered (same stream); the read-add-write is not atomic across concurrent calls.
+ */
+enum { ATTN_ACC_DQ = 1, ATTN_ACC_DKDV = 2 };
+int attn_bwd_accum(int B, int Sq, int Sk, int H, int D, float scale, const void* q,
+                   const void* k, const void* v, const uint8_t* key_mask, const float* lse,
+                   const float* delta, const void* dout, float* dq_acc, float* dk_acc,
+                   float* dv_acc, int flags, void* stream);
+
+/* dst[i] = bf16(src[i]), round to nearest even, for n fp32 values (device pointers). */
+int attn_cast_bf16(int64_t n, const float* src, void* dst, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

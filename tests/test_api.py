@@ -34,17 +34,19 @@ def declared():
 def test_exports_every_declared_symbol(L):
     names = declared()
     assert {"attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_varlen_fwd",
-            "attn_varlen_bwd"} <= set(names)
+            "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum", "attn_cast_bf16"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 1
+    assert L.attn_abi_version() == 2
     assert L.attn_status_str(0) == b"ok"
     assert L.attn_status_str(4) == b"invalid cu_seqlens"
 
 
 def test_status_enum_matches_header():
     text = open(HEADER).read()
-    enum = dict((k, int(v)) for k, v in re.findall(r"(ATTN_\w+)\s*=\s*(\d+)", text))
+    block = re.search(r"typedef\s+enum\s*\{(.*?)\}\s*attn_status\s*;", text, re.S)
+    assert block, "attn_status enum not found"
+    enum = dict((k, int(v)) for k, v in re.findall(r"(ATTN_\w+)\s*=\s*(\d+)", block.group(1)))
     assert {v: k for k, v in enum.items()} == A.STATUS
 
 
@@ -89,6 +91,46 @@ def test_preprocess_and_bwd_validation(L):
     a = list(args)
     a[0] = 0
     assert L.attn_bwd(*a) == OK
+
+
+def test_merge_accum_cast_validation(L):
+    n2 = (ctypes.c_void_p * 2)(P.value, P.value)
+    n1null = (ctypes.c_void_p * 2)(P.value, None)
+
+    def merge(n=2, B=1, S=8, H=2, D=128, outs=n2, lses=n2, out=P, lse=P):
+        return L.attn_lse_merge(n, B, S, H, D, outs, lses, out, lse, None)
+
+    assert merge(n=0) == SHAPE
+    assert merge(n=17) == UNSUP
+    assert merge(B=-1) == SHAPE
+    assert merge(D=96) == UNSUP
+    assert merge(outs=None) == NULL
+    assert merge(lses=n1null) == NULL
+    assert merge(out=None) == NULL
+    assert merge(B=0, outs=n1null, lses=n1null, out=None, lse=None) == OK  # nothing to merge
+
+    args = [1, 8, 8, 2, 64, 0.125, P, P, P, None, P, P, P, P, P, P, 3, None]
+    for i in (6, 7, 8, 10, 11, 12, 13, 14, 15):
+        a = list(args)
+        a[i] = None
+        assert L.attn_bwd_accum(*a) == NULL, i
+    a = list(args)
+    a[16] = 4  # unknown flag bit
+    assert L.attn_bwd_accum(*a) == SHAPE
+    a = list(args)
+    a[4] = 96
+    assert L.attn_bwd_accum(*a) == UNSUP
+    a = list(args)
+    a[5] = 0.0
+    assert L.attn_bwd_accum(*a) == SHAPE
+    a = list(args)
+    a[3] = 0
+    assert L.attn_bwd_accum(*a) == OK
+
+    assert L.attn_cast_bf16(-1, P, P, None) == SHAPE
+    assert L.attn_cast_bf16(4, None, P, None) == NULL
+    assert L.attn_cast_bf16(4, P, None, None) == NULL
+    assert L.attn_cast_bf16(0, None, None, None) == OK
 
 
 def _cu(vals):
