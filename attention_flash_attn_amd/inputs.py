@@ -63,6 +63,11 @@ class Workload:
     valid_lens: Optional[Sequence[int]] = None  # per-batch key prefix lengths (mask)
     seqlens: Optional[Sequence[int]] = None  # varlen sequence lengths (packed)
     seed: int = 0
+    Hk: Optional[int] = None  # key/value heads (grouped-query attention); None = H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hk is None else self.Hk
 
     @property
     def varlen(self) -> bool:
@@ -79,6 +84,10 @@ class Workload:
     @property
     def shape(self):
         return (1, self.T, self.H, self.D) if self.varlen else (self.B, self.S, self.H, self.D)
+
+    @property
+    def kv_shape(self):
+        return self.shape[:2] + (self.kv_heads, self.D)
 
     def cu_seqlens(self) -> Optional[np.ndarray]:
         if not self.varlen:
@@ -110,6 +119,9 @@ WORKLOADS = {
     "mask_s4096": Workload("mask_s4096", B=2, S=4096, H=24, D=128, valid_lens=(3001, 4096), seed=3),
     "wan_shard": Workload("wan_shard", B=1, S=27280, H=10, D=128, seed=4),
     "varlen4": Workload("varlen4", B=1, S=27330, H=24, D=128, seqlens=(4096, 7000, 1234, 15000), seed=5),
+    # Grouped-query attention (named as not yet extended in diffusers PR #14834, description;
+    # the pages give no GQA workload): the Wan shard's query heads over 2 key/value heads.
+    "wan_shard_gqa": Workload("wan_shard_gqa", B=1, S=27280, H=10, D=128, seed=6, Hk=2),
 }
 
 
@@ -125,27 +137,32 @@ class Tensors:
     cu_seqlens: Optional[np.ndarray]
 
 
-def draw(shape, seed: int, key_mask=None, cu_seqlens=None) -> Tensors:
-    """Draw q, k, v, dO i.i.d. N(0,1) (in that order) and round each to bf16."""
+def draw(shape, seed: int, key_mask=None, cu_seqlens=None, kv_shape=None) -> Tensors:
+    """Draw q, k, v, dO i.i.d. N(0,1) (in that order) and round each to bf16; k and v take
+    kv_shape when given (fewer key/value heads)."""
     rng = np.random.default_rng(seed)
     out = []
-    for _ in range(4):
-        out.append(bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32)))
+    for i in range(4):
+        shp = kv_shape if (kv_shape is not None and i in (1, 2)) else shape
+        out.append(bf16_bits_from_f32(rng.standard_normal(shp, dtype=np.float32)))
     return Tensors(out[0], out[1], out[2], out[3], key_mask, cu_seqlens)
 
 
 def draw_workload(w: Workload, seed: Optional[int] = None) -> Tensors:
-    return draw(w.shape, w.seed if seed is None else seed, w.key_mask(), w.cu_seqlens())
+    return draw(w.shape, w.seed if seed is None else seed, w.key_mask(), w.cu_seqlens(),
+                w.kv_shape if w.Hk is not None else None)
 
 
-def small_case(B, Sq, Sk, H, D, seed, valid_lens=None):
-    """Dense inputs with Sq != Sk allowed: q/dO get Sq rows, k/v get Sk rows.
+def small_case(B, Sq, Sk, H, D, seed, valid_lens=None, Hk=None):
+    """Dense inputs with Sq != Sk allowed: q/dO get Sq rows, k/v get Sk rows (and Hk heads
+    when given).
 
     Draw order is still q, k, v, dO."""
     rng = np.random.default_rng(seed)
+    Hk = H if Hk is None else Hk
     q = bf16_bits_from_f32(rng.standard_normal((B, Sq, H, D), dtype=np.float32))
-    k = bf16_bits_from_f32(rng.standard_normal((B, Sk, H, D), dtype=np.float32))
-    v = bf16_bits_from_f32(rng.standard_normal((B, Sk, H, D), dtype=np.float32))
+    k = bf16_bits_from_f32(rng.standard_normal((B, Sk, Hk, D), dtype=np.float32))
+    v = bf16_bits_from_f32(rng.standard_normal((B, Sk, Hk, D), dtype=np.float32))
     do = bf16_bits_from_f32(rng.standard_normal((B, Sq, H, D), dtype=np.float32))
     mask = None
     if valid_lens is not None:

@@ -171,3 +171,34 @@ def attn_lse_merge(outs, lses):
     lp = (_dp * n)(*[_p(l) for l in lses])
     _check(_load().oracle_attn_lse_merge(n, B, S, H, D, op, lp, _p(out), _p(lse)))
     return out, lse
+
+
+# ---------------------------------------------------------------- grouped-query attention
+#
+# GQA (diffusers PR #14834 names it as not extended; the cuDNN / flash messages quoted in
+# diffusers PR #14341, reporter's tables, state the constraint that the key/value head count
+# divides the query head count).  Query head h reads key/value head h // G, G = H / Hk.
+# Written out as its definition: attention with each key/value head repeated over its
+# group of G query heads; the gradient of a repeated tensor is the sum of the gradients of
+# its copies (chain rule), so dK, dV of head g sum the G expanded heads' dK, dV.
+
+
+def _gqa_group(H, Hk):
+    assert Hk >= 1 and H % Hk == 0, (H, Hk)
+    return H // Hk
+
+
+def attn_fwd_gqa(q, k, v, key_mask=None, scale=None):
+    """q (B,Sq,H,D), k/v (B,Sk,Hk,D) -> out (B,Sq,H,D), lse (B,H,Sq)."""
+    G = _gqa_group(q.shape[2], k.shape[2])
+    return attn_fwd(q, np.repeat(_f64(k), G, axis=2), np.repeat(_f64(v), G, axis=2), key_mask, scale)
+
+
+def attn_bwd_gqa(q, k, v, out, lse, dout, key_mask=None, scale=None):
+    """-> (delta, dq (B,Sq,H,D), dk, dv (B,Sk,Hk,D))."""
+    B, Sk, Hk, D = k.shape
+    G = _gqa_group(q.shape[2], Hk)
+    delta, dq, dke, dve = attn_bwd(q, np.repeat(_f64(k), G, axis=2), np.repeat(_f64(v), G, axis=2),
+                                   out, lse, dout, key_mask, scale)
+    return (delta, dq, dke.reshape(B, Sk, Hk, G, D).sum(axis=3),
+            dve.reshape(B, Sk, Hk, G, D).sum(axis=3))
