@@ -53,11 +53,13 @@ def lib():
     L.attn_varlen_fwd.argtypes = [i, vp, vp, i, i, f, vp, vp, vp, vp, vp, vp]
     L.attn_varlen_bwd.argtypes = [i, vp, vp, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_lse_merge.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp]
+    L.attn_fwd_gqa.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_bwd_gqa.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_bwd_accum.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.attn_cast_bf16.argtypes = [ctypes.c_int64, vp, vp, vp]
     for name in ("attn_abi_version", "attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                  "attn_varlen_fwd", "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum",
-                 "attn_cast_bf16"):
+                 "attn_cast_bf16", "attn_fwd_gqa", "attn_bwd_gqa"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -125,13 +127,24 @@ def _dims(q, k):
     return B, Sq, Sk, H, D
 
 
+def _kv_heads(q, k):
+    """Key/value heads of k (grouped-query attention when fewer than q's heads)."""
+    H, Hk = q.shape[2], k.shape[2]
+    if Hk < 1 or H % Hk:
+        raise ValueError(f"k/v have {Hk} heads, which must divide the {H} query heads")
+    return Hk
+
+
 def attn_fwd(q, k, v, key_mask=None, scale=None, out=None, lse=None):
-    """out, lse = attn_fwd(q, k, v): q (B,Sq,H,D), k/v (B,Sk,H,D) bf16 -> out bf16, lse fp32 (B,H,Sq)."""
+    """out, lse = attn_fwd(q, k, v): q (B,Sq,H,D), k/v (B,Sk,Hk,D) bf16 (Hk dividing H:
+    grouped-query attention, query head h reading key/value head h // (H/Hk))
+    -> out bf16, lse fp32 (B,H,Sq)."""
     torch = _torch()
     B, Sq, Sk, H, D = _dims(q, k)
+    Hk = _kv_heads(q, k)
     _want(q, "q", (B, Sq, H, D), torch.bfloat16)
-    _want(k, "k", (B, Sk, H, D), torch.bfloat16)
-    _want(v, "v", (B, Sk, H, D), torch.bfloat16)
+    _want(k, "k", (B, Sk, Hk, D), torch.bfloat16)
+    _want(v, "v", (B, Sk, Hk, D), torch.bfloat16)
     m = _mask_arg(key_mask, B, Sk, H)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
@@ -140,8 +153,8 @@ def attn_fwd(q, k, v, key_mask=None, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     _want(out, "out", (B, Sq, H, D), torch.bfloat16)
     _want(lse, "lse", (B, H, Sq), torch.float32)
-    _check("attn_fwd", lib().attn_fwd(B, Sq, Sk, H, D, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(m),
-                                      _ptr(out), _ptr(lse), _stream()))
+    _check("attn_fwd", lib().attn_fwd_gqa(B, Sq, Sk, H, Hk, D, scale, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(m), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 
@@ -162,12 +175,14 @@ def attn_bwd_preprocess(out, dout, delta=None):
 
 
 def attn_bwd(q, k, v, lse, delta, dout, key_mask=None, scale=None, dq=None, dk=None, dv=None):
-    """dq, dk, dv = attn_bwd(q, k, v, lse, delta, dout) (bf16 BSHD grads)."""
+    """dq, dk, dv = attn_bwd(q, k, v, lse, delta, dout) (bf16 BSHD grads; dk, dv have k's
+    Hk heads, each summing its query heads' contributions)."""
     torch = _torch()
     B, Sq, Sk, H, D = _dims(q, k)
+    Hk = _kv_heads(q, k)
     _want(q, "q", (B, Sq, H, D), torch.bfloat16)
-    _want(k, "k", (B, Sk, H, D), torch.bfloat16)
-    _want(v, "v", (B, Sk, H, D), torch.bfloat16)
+    _want(k, "k", (B, Sk, Hk, D), torch.bfloat16)
+    _want(v, "v", (B, Sk, Hk, D), torch.bfloat16)
     _want(dout, "dout", (B, Sq, H, D), torch.bfloat16)
     _want(lse, "lse", (B, H, Sq), torch.float32)
     _want(delta, "delta", (B, H, Sq), torch.float32)
@@ -177,11 +192,11 @@ def attn_bwd(q, k, v, lse, delta, dout, key_mask=None, scale=None, dq=None, dk=N
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _want(dq, "dq", (B, Sq, H, D), torch.bfloat16)
-    _want(dk, "dk", (B, Sk, H, D), torch.bfloat16)
-    _want(dv, "dv", (B, Sk, H, D), torch.bfloat16)
-    _check("attn_bwd", lib().attn_bwd(B, Sq, Sk, H, D, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(m),
-                                      _ptr(lse), _ptr(delta), _ptr(dout), _ptr(dq), _ptr(dk),
-                                      _ptr(dv), _stream()))
+    _want(dk, "dk", (B, Sk, Hk, D), torch.bfloat16)
+    _want(dv, "dv", (B, Sk, Hk, D), torch.bfloat16)
+    _check("attn_bwd", lib().attn_bwd_gqa(B, Sq, Sk, H, Hk, D, scale, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(m), _ptr(lse), _ptr(delta), _ptr(dout), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _stream()))
     return dq, dk, dv
 
 

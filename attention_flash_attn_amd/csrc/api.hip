@@ -15,7 +15,7 @@ using attn::FwdParams;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
 // The backward starts its score accumulators from -LSE/scale; the lower bound keeps that
@@ -35,6 +35,14 @@ int check_dense(int B, int Sq, int Sk, int H, int D, float scale) {
   if ((long)B * Sq > INT_MAX || (long)B * Sk > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   if ((cdiv(Sq, 32) + cdiv(Sk, 32)) * H * (long)B > INT_MAX)
     return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// Key/value head count of grouped-query attention: it divides H (H = G * Hk, G >= 1).
+int check_kv_heads(int H, int Hk) {
+  if (Hk < 0) return ATTN_ERR_SHAPE;
+  if (H == 0) return Hk == 0 ? ATTN_OK : ATTN_ERR_SHAPE;
+  if (Hk == 0 || H % Hk != 0) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -76,9 +84,16 @@ int attn_abi_version(void) { return kAbiVersion; }
 
 int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, void* out, float* lse, void* stream) {
-  const int st = check_dense(B, Sq, Sk, H, D, scale);
+  return attn_fwd_gqa(B, Sq, Sk, H, H, D, scale, q, k, v, key_mask, out, lse, stream);
+}
+
+int attn_fwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
+                 const void* k, const void* v, const uint8_t* key_mask, void* out, float* lse,
+                 void* stream) {
+  int st = check_dense(B, Sq, Sk, H, D, scale);
+  if (st == ATTN_OK) st = check_kv_heads(H, Hk);
   if (st != ATTN_OK) return st;
-  const bool has_q = (long)B * Sq * H > 0, has_k = (long)B * Sk * H > 0;
+  const bool has_q = (long)B * Sq * H > 0, has_k = (long)B * Sk * Hk > 0;
   if (missing(q, has_q) || missing(out, has_q) || missing(lse, has_q) || missing(k, has_k) ||
       missing(v, has_k))
     return ATTN_ERR_NULL;
@@ -95,6 +110,8 @@ int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, co
   p.Sq = Sq;
   p.Sk = Sk;
   p.H = H;
+  p.Hk = Hk;
+  p.G = H / Hk;
   p.n_qtiles = (int)cdiv(Sq, attn::kFwdBlockM);
   p.n_blocks = p.n_qtiles * H * B;
   p.c2 = scale * attn::kLog2e;
@@ -115,11 +132,13 @@ int attn_bwd_preprocess(int B, int S, int H, int D, const void* out, const void*
                                       static_cast<hipStream_t>(stream)));
 }
 
-static BwdParams bwd_params(int B, int Sq, int Sk, int H, float scale, const void* q,
+static BwdParams bwd_params(int B, int Sq, int Sk, int H, int Hk, float scale, const void* q,
                             const void* k, const void* v, const uint8_t* key_mask,
                             const float* lse, const float* delta, const void* dout, void* dq,
                             void* dk, void* dv, const int32_t* cu) {
   BwdParams p{};
+  p.Hk = Hk;
+  p.G = Hk > 0 ? H / Hk : 1;
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);
   p.v = static_cast<const __bf16*>(v);
@@ -140,22 +159,39 @@ static BwdParams bwd_params(int B, int Sq, int Sk, int H, float scale, const voi
   return p;
 }
 
+// Grid of the backward launch: per (outer, key/value head) the dQ workgroups of its G query
+// heads and its dK/dV workgroups, the longer kind first.  Work per workgroup: dK/dV 128 keys
+// x G * nq query rows x 4 products, dQ 256 query rows x nk keys x 3 products.
+static void bwd_grid(BwdParams& p, int nq, int nk, int outer) {
+  p.n_kv_tiles = (int)cdiv(nk, attn::kDkvBlockN);
+  p.n_q_tiles = (int)cdiv(nq, attn::kDqBlockM);
+  p.dkdv_first = (long)attn::kDkvBlockN * 4 * p.G * nq > (long)attn::kDqBlockM * 3 * nk;
+  p.n_blocks = (p.n_kv_tiles + p.G * p.n_q_tiles) * p.Hk * outer;
+}
+
 int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, const float* lse, const float* delta,
              const void* dout, void* dq, void* dk, void* dv, void* stream) {
-  const int st = check_dense(B, Sq, Sk, H, D, scale);
+  return attn_bwd_gqa(B, Sq, Sk, H, H, D, scale, q, k, v, key_mask, lse, delta, dout, dq, dk, dv,
+                      stream);
+}
+
+int attn_bwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
+                 const void* k, const void* v, const uint8_t* key_mask, const float* lse,
+                 const float* delta, const void* dout, void* dq, void* dk, void* dv,
+                 void* stream) {
+  int st = check_dense(B, Sq, Sk, H, D, scale);
+  if (st == ATTN_OK) st = check_kv_heads(H, Hk);
   if (st != ATTN_OK) return st;
-  const bool hq = (long)B * Sq * H > 0, hk = (long)B * Sk * H > 0;
+  const bool hq = (long)B * Sq * H > 0, hk = (long)B * Sk * Hk > 0;
   if (missing(q, hq) || missing(lse, hq) || missing(delta, hq) || missing(dout, hq) ||
       missing(dq, hq) || missing(k, hk) || missing(v, hk) || missing(dk, hk) || missing(dv, hk))
     return ATTN_ERR_NULL;
   if ((long)B * H == 0) return ATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  BwdParams p = bwd_params(B, Sq, Sk, H, scale, q, k, v, key_mask, lse, delta, dout, dq, dk, dv,
-                           nullptr);
-  p.n_kv_tiles = (int)cdiv(Sk, attn::kDkvBlockN);
-  p.n_q_tiles = (int)cdiv(Sq, attn::kDqBlockM);
-  p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * B;
+  BwdParams p = bwd_params(B, Sq, Sk, H, Hk, scale, q, k, v, key_mask, lse, delta, dout, dq, dk,
+                           dv, nullptr);
+  bwd_grid(p, Sq, Sk, B);
   return status_of(attn::launch_bwd(D, false, false, p, s));
 }
 
@@ -172,15 +208,13 @@ int attn_bwd_accum(int B, int Sq, int Sk, int H, int D, float scale, const void*
       missing(dv_acc, hk))
     return ATTN_ERR_NULL;
   if ((long)B * H == 0) return ATTN_OK;
-  BwdParams p = bwd_params(B, Sq, Sk, H, scale, q, k, v, key_mask, lse, delta, dout, nullptr,
+  BwdParams p = bwd_params(B, Sq, Sk, H, H, scale, q, k, v, key_mask, lse, delta, dout, nullptr,
                            nullptr, nullptr, nullptr);
   p.dq_acc = dq_acc;
   p.dk_acc = dk_acc;
   p.dv_acc = dv_acc;
   p.acc_flags = flags;
-  p.n_kv_tiles = (int)cdiv(Sk, attn::kDkvBlockN);
-  p.n_q_tiles = (int)cdiv(Sq, attn::kDqBlockM);
-  p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * B;
+  bwd_grid(p, Sq, Sk, B);
   return status_of(attn::launch_bwd(D, false, true, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -240,6 +274,8 @@ int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
   p.B = nseq;
   p.Sq = p.Sk = T;
   p.H = H;
+  p.Hk = H;
+  p.G = 1;
   p.n_qtiles = (int)cdiv(maxlen, attn::kFwdBlockM);
   p.n_blocks = p.n_qtiles * H * nseq;
   p.c2 = scale * attn::kLog2e;
@@ -261,11 +297,9 @@ int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
     return ATTN_ERR_NULL;
   if ((long)T * H == 0) return ATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  BwdParams p = bwd_params(nseq, T, T, H, scale, q, k, v, nullptr, lse, delta, dout, dq, dk, dv,
-                           cu_seqlens_dev);
-  p.n_kv_tiles = (int)cdiv(maxlen, attn::kDkvBlockN);
-  p.n_q_tiles = (int)cdiv(maxlen, attn::kDqBlockM);
-  p.n_blocks = (p.n_kv_tiles + p.n_q_tiles) * H * nseq;
+  BwdParams p = bwd_params(nseq, T, T, H, H, scale, q, k, v, nullptr, lse, delta, dout, dq, dk,
+                           dv, cu_seqlens_dev);
+  bwd_grid(p, maxlen, maxlen, nseq);
   return status_of(attn::launch_bwd(D, true, false, p, s));
 }
 

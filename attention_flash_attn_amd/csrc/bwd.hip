@@ -31,8 +31,9 @@
 // matrix instructions run while the other does its exponentials and conversions (a wave
 // does not overlap the two itself).
 //
-// Both run in ONE launch: the grid is grouped per (batch|sequence, head), each group
-// holding that head's dQ workgroups followed by its dK/dV workgroups, and groups
+// Both run in ONE launch: the grid is grouped per (batch|sequence, key/value head), each
+// group holding the dQ workgroups of its query heads and its dK/dV workgroups (the longer
+// kind first), and groups
 // are dealt to XCDs in contiguous ranges.  Every XCD therefore gets the same mix
 // of the two workgroup kinds, and the two kinds of one head share its Q/K/V/dO
 // in that XCD's L2.
@@ -83,32 +84,35 @@ hipError_t launch_delta(int D, long rows, int S, int H, const bf16* out, const b
   return hipLaunchKernel(fn, dim3((unsigned)nb), dim3(256), args, 0, stream);
 }
 
-// Shared decode of (tile, head, outer) and the row ranges of one workgroup.
+// Shared decode of one workgroup: its tile, (outer, key/value head) group, query head
+// (query head i of the group: kvhead * G + i) and row ranges.  The LSE / delta rows of
+// query head h + 1 follow those of head h at a distance of p.Sq in both layouts.
 struct Slice {
-  int tile, head, qrow0, krow0, nq, nk;
-  long lse_base;
+  int tile, qhead, kvhead, qrow0, krow0, nq, nk;
+  long lse_base;  // of qhead
   const uint8_t* mask;
 };
 
 template <bool VARLEN>
-__device__ __forceinline__ Slice decode(const BwdParams& p, int group, int tile) {
+__device__ __forceinline__ Slice decode(const BwdParams& p, int group, int tile, int i) {
   Slice s;
   s.tile = tile;
   // head-major groups: equal work per XCD range when sequences differ (see fwd.hip)
-  s.head = group / p.B;
+  s.kvhead = group / p.B;
+  s.qhead = s.kvhead * p.G + i;
   const int outer = group % p.B;
   s.mask = nullptr;
   if (VARLEN) {
     const int s0 = p.cu[outer], s1 = p.cu[outer + 1];
     s.qrow0 = s.krow0 = s0;
     s.nq = s.nk = s1 - s0;
-    s.lse_base = (long)s.head * p.Sq + s0;
+    s.lse_base = (long)s.qhead * p.Sq + s0;
   } else {
     s.qrow0 = outer * p.Sq;
     s.krow0 = outer * p.Sk;
     s.nq = p.Sq;
     s.nk = p.Sk;
-    s.lse_base = ((long)outer * p.H + s.head) * p.Sq;
+    s.lse_base = ((long)outer * p.H + s.qhead) * p.Sq;
     if (p.mask) s.mask = p.mask + (long)outer * p.Sk;
   }
   return s;
@@ -184,7 +188,10 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   const int kblk = wave & 3, sub = wave >> 2;
   const int kb0 = sl.tile * BN;
   if (kb0 >= sl.nk) return;  // block-uniform
-  const long rs = (long)p.H * D;
+  // Q/dO rows hold H heads, K/V/dK/dV rows Hk.  The loop runs over the query tiles of all
+  // G query heads that read this key/value head (query head qhead + i for i < G), so dK
+  // and dV sum their contributions (grouped-query attention) without atomics.
+  const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int nq = sl.nq, nk = sl.nk;
 
   const int key = kb0 + 32 * kblk + l32;
@@ -199,15 +206,15 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 
   auto same_row = [](int r) { return r; };
   auto qrow_of = [](int r) { return perm32_row(r); };
-  const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
-  const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
-  const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.head * D;
-  const bf16* obase = p.dout + (long)sl.qrow0 * rs + (long)sl.head * D;
+  const bf16* kbase = p.k + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
+  const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
+  const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.qhead * D;
+  const bf16* obase = p.dout + (long)sl.qrow0 * rs + (long)sl.qhead * D;
   {
     TileLoader<D, BN, NW> kvld;
-    kvld.init(rs, same_row);
-    kvld.issue(sm.k, kbase, rs, kb0, nk, same_row);
-    kvld.issue(sm.v, vbase, rs, kb0, nk, same_row);
+    kvld.init(rsk, same_row);
+    kvld.issue(sm.k, kbase, rsk, kb0, nk, same_row);
+    kvld.issue(sm.v, vbase, rsk, kb0, nk, same_row);
   }
   TileLoader<D, BQ, 4> ld;  // used by waves 0..3
   ld.init(rs, qrow_of);
@@ -215,22 +222,26 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   // its asynchronous copy and only used when published after the current tile's
   // compute: a use right after the load would make the wave wait for the whole copy.
   float lraw = 0.f, draw = 0.f;
-  auto issue = [&](int q0, char* qt, char* ot) {
-    const long qi = sl.lse_base + min(q0 + lane, nq - 1);
+  const int ntq = (nq + BQ - 1) / BQ;  // query tiles per query head
+  // Tile t of the loop: query head qhead + t / ntq, rows (t % ntq) * BQ ...
+  auto issue = [&](int t, char* qt, char* ot) {
+    const int i = t / ntq, q0 = (t - i * ntq) * BQ;
+    const long qi = sl.lse_base + (long)i * p.Sq + min(q0 + lane, nq - 1);
     lraw = p.lse[qi];
     draw = p.delta[qi];
     // Only the sub-tile-0 waves copy: right after the barrier the copies queue up in the
     // memory pipeline and stall the waves that issue them (32 KB at ~64 B/clock), and
     // meanwhile the sub-tile-1 wave of each SIMD has its matrix unit to itself.
     if (sub == 0) {
-      ld.issue(qt, qbase, rs, q0, nq, qrow_of);
-      ld.issue(ot, obase, rs, q0, nq, qrow_of);
+      ld.issue(qt, qbase + (long)i * D, rs, q0, nq, qrow_of);
+      ld.issue(ot, obase + (long)i * D, rs, q0, nq, qrow_of);
     }
   };
   // Published per row: -LSE/scale and -delta, the starting values of the S and dP
   // accumulators (rows past the end get -inf, so their P is 0).
   const float nis = -1.f / p.scale;
-  auto publish_stats = [&](int q0, float* lt, float* dt) {
+  auto publish_stats = [&](int t, float* lt, float* dt) {
+    const int q0 = (t - (t / ntq) * ntq) * BQ;
     if (tid < BQ) {
       const bool in = q0 + tid < nq;
       lt[tid] = in ? lraw * nis : -INFINITY;
@@ -276,7 +287,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     }
   };
 
-  const int ntiles = (nq + BQ - 1) / BQ;
+  const int ntiles = p.G * ntq;
   // All tile buffers are distinct __restrict__ parameters, so once inlined the compiler
   // can tell reads of the current tile from the asynchronous copy into the next one
   // (without that it waits for the copy before the first LDS read).
@@ -285,10 +296,9 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
                   const float* __restrict__ cl, const float* __restrict__ cd, char* __restrict__ nq_,
                   char* __restrict__ no_, float* __restrict__ nl, float* __restrict__ nd) {
     const bool more = j + 1 < ntiles;
-    const int q1 = (j + 1) * BQ;
-    if (more) issue(q1, nq_, no_);
+    if (more) issue(j + 1, nq_, no_);
     if (kball != 0) compute(kt, vt, cq, co, cl, cd);
-    if (more) publish_stats(q1, nl, nd);
+    if (more) publish_stats(j + 1, nl, nd);
     wait_tile_loads();
     __syncthreads();
   };
@@ -319,7 +329,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   }
   __syncthreads();
   if (sub == 0 && key < nk) {
-    const long off = ((long)sl.krow0 + key) * rs + (long)sl.head * D + 4 * hl;
+    const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * hl;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -364,13 +374,14 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const int hl = lane >> 5, l32 = lane & 31;
   const int qb = sl.tile * BM;
   if (qb >= sl.nq) return;  // block-uniform
-  const long rs = (long)p.H * D;
+  // Q/dO/dQ rows hold H heads, K/V rows Hk (this query head reads key/value head kvhead).
+  const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int nq = sl.nq, nk = sl.nk;
 
   const int qrow = qb + wave * 32 + l32;
   bf16x8 qreg[NKS], doreg[NKS];
   {
-    const long off = ((long)sl.qrow0 + min(qrow, nq - 1)) * rs + (long)sl.head * D + 8 * hl;
+    const long off = ((long)sl.qrow0 + min(qrow, nq - 1)) * rs + (long)sl.qhead * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       qreg[ks] = as_bf16x8(ld16(p.q + off + 16 * ks));
@@ -403,17 +414,17 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     }
   };
 
-  const bf16* kbase = p.k + (long)sl.krow0 * rs + (long)sl.head * D;
-  const bf16* vbase = p.v + (long)sl.krow0 * rs + (long)sl.head * D;
+  const bf16* kbase = p.k + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
+  const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   auto krow_of = [](int r) { return perm32_row(r); };
   TileLoader<D, BN, 4> ld;  // used by waves 0..3
-  ld.init(rs, krow_of);
+  ld.init(rsk, krow_of);
   // Only waves 0..3 copy (see dkdv_block): while they stall at issue, waves 4..7, one per
   // SIMD, keep the matrix units busy.
   auto issue = [&](int k0, char* kt, char* vt) {
     if (wave < 4) {
-      ld.issue(kt, kbase, rs, k0, nk, krow_of);
-      ld.issue(vt, vbase, rs, k0, nk, krow_of);
+      ld.issue(kt, kbase, rsk, k0, nk, krow_of);
+      ld.issue(vt, vbase, rsk, k0, nk, krow_of);
     }
   };
 
@@ -512,7 +523,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   }
 
   if (qrow < nq) {
-    const long off = ((long)sl.qrow0 + qrow) * rs + (long)sl.head * D + 4 * hl;
+    const long off = ((long)sl.qrow0 + qrow) * rs + (long)sl.qhead * D + 4 * hl;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -533,7 +544,8 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 }
 
 // One launch for the whole backward.  Logical workgroup ids are grouped per
-// (outer, head): [dQ tiles of that head][dK/dV tiles of that head].
+// (outer, key/value head): [dQ tiles of its query heads][its dK/dV tiles], or the
+// other way round when the dK/dV workgroups are the longer ones.
 template <int D, bool VARLEN, bool ACC>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   union Smem {
@@ -542,13 +554,30 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int logical = xcd_remap(blockIdx.x, p.n_blocks);
-  const int per_group = p.n_kv_tiles + p.n_q_tiles;
+  // A group is one (outer, key/value head): the dQ workgroups of its G query heads and its
+  // dK/dV workgroups, the longer kind first (host-chosen) so that the grid's tail holds the
+  // shorter ones.
+  const int nqw = p.G * p.n_q_tiles;
+  const int per_group = p.n_kv_tiles + nqw;
   const int group = logical / per_group, within = logical % per_group;
-  // dQ workgroups (the longer ones) first, so the grid's tail holds the shorter dK/dV ones.
-  if (within >= p.n_q_tiles)
-    dkdv_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, within - p.n_q_tiles), sm.kv);
+  bool kv;
+  int idx;
+  if (p.G > 1) {
+    // Grouped-query attention: few, large groups (one per key/value head), each of them
+    // spanning several XCD ranges, so the two kinds are interleaved evenly inside the
+    // group: position w is a dK/dV workgroup iff floor((w+1) n_kv / n) steps up there.
+    const int d1 = (int)((long)(within + 1) * p.n_kv_tiles / per_group);
+    const int d0 = (int)((long)within * p.n_kv_tiles / per_group);
+    kv = d1 > d0;
+    idx = kv ? d0 : within - d1;
+  } else {
+    kv = p.dkdv_first ? within < p.n_kv_tiles : within >= nqw;
+    idx = kv ? (p.dkdv_first ? within : within - nqw) : (p.dkdv_first ? within - p.n_kv_tiles : within);
+  }
+  if (kv)
+    dkdv_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, idx, 0), sm.kv);
   else
-    dq_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, within), sm.q);
+    dq_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, idx % p.n_q_tiles, idx / p.n_q_tiles), sm.q);
 }
 
 template <int D, bool VARLEN, bool ACC>

@@ -70,9 +70,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int qb = qt * BM;
   if (qb >= nq) return;  // block-uniform: a varlen tile past its sequence
 
-  const long rs = (long)p.H * D;
-  const bf16* kbase = p.k + (long)krow0 * rs + (long)head * D;
-  const bf16* vbase = p.v + (long)krow0 * rs + (long)head * D;
+  // Q/out rows hold H heads, K/V rows Hk; query head h reads key/value head h / G.
+  const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
+  const int kvh = head / p.G;
+  const bf16* kbase = p.k + (long)krow0 * rsk + (long)kvh * D;
+  const bf16* vbase = p.v + (long)krow0 * rsk + (long)kvh * D;
 
   // Query rows of this wave, as B operand slices over the head dim.
   const int qrow = qb + wave * 32 + l32;
@@ -101,11 +103,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   TileLoader<D, BN, 4> kld, vld;
   auto krow = [](int r) { return perm32_row(r); };
   auto vrow = [](int r) { return r; };
-  kld.init(rs, krow);
-  vld.init(rs, vrow);
+  kld.init(rsk, krow);
+  vld.init(rsk, vrow);
   auto issue = [&](int k0, char* kt, char* vt) {
-    kld.issue(kt, kbase, rs, k0, nk, krow);
-    vld.issue(vt, vbase, rs, k0, nk, vrow);
+    kld.issue(kt, kbase, rsk, k0, nk, krow);
+    vld.issue(vt, vbase, rsk, k0, nk, vrow);
   };
 
   f32x16 oacc[NMB];

@@ -16,6 +16,7 @@ struct FwdParams {
   float* lse;
   const int32_t* cu;  // varlen only (device)
   int B, Sq, Sk, H;
+  int Hk, G;     // key/value heads and query heads per key/value head (H = G * Hk)
   int n_qtiles;  // query tiles per (outer, head)
   int n_blocks;
   float c2;  // scale * log2(e)
@@ -38,8 +39,10 @@ struct BwdParams {
   int acc_flags;  // bit 0: add into dq_acc, bit 1: add into dk_acc/dv_acc (else overwrite)
   const int32_t* cu;
   int B, Sq, Sk, H;
-  int n_kv_tiles;  // dK/dV workgroups per (outer, head)
-  int n_q_tiles;   // dQ workgroups per (outer, head)
+  int Hk, G;       // key/value heads and query heads per key/value head (H = G * Hk)
+  int n_kv_tiles;  // dK/dV workgroups per (outer, key/value head)
+  int n_q_tiles;   // dQ workgroups per (outer, query head)
+  int dkdv_first;  // grid order inside a group: the longer workgroup kind first
   int n_blocks;
   float c2;     // scale * log2(e)
   float scale;

@@ -96,6 +96,23 @@ int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, co
              const void* dout, void* dq, void* dk, void* dv, void* stream);
 
 /*
+ * Grouped-query attention (named as not yet extended in diffusers PR #14834, description;
+ * the key/value head count must divide the query head count, as the flash / cuDNN errors
+ * quoted in diffusers PR #14341, reporter's tables, state): as attn_fwd / attn_bwd, but k
+ * and v (and dk, dv) are (B,Sk,Hk,D) with H = G * Hk, and query head h attends with key /
+ * value head h / G.  dk, dv of a key/value head sum the contributions of its G query heads
+ * (computed in one workgroup per key tile, no atomics, bitwise reproducible).  Hk that does
+ * not divide H: ATTN_ERR_SHAPE.  attn_fwd / attn_bwd are these calls with Hk = H.
+ */
+int attn_fwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
+                 const void* k, const void* v, const uint8_t* key_mask, void* out, float* lse,
+                 void* stream);
+int attn_bwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
+                 const void* k, const void* v, const uint8_t* key_mask, const float* lse,
+                 const float* delta, const void* dout, void* dq, void* dk, void* dv,
+                 void* stream);
+
+/*
  * Packed variable-length forward (the FA3-varlen path of diffusers PR #14834,
  * "Model test coverage"): nseq sequences packed back to back in q, k, v
  * (T, H, D); sequence n owns rows [cu[n], cu[n+1]) and attends only to its own

@@ -34,10 +34,11 @@ def declared():
 def test_exports_every_declared_symbol(L):
     names = declared()
     assert {"attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_varlen_fwd",
-            "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum", "attn_cast_bf16"} <= set(names)
+            "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum", "attn_cast_bf16",
+            "attn_fwd_gqa", "attn_bwd_gqa"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 2
+    assert L.attn_abi_version() == 3
     assert L.attn_status_str(0) == b"ok"
     assert L.attn_status_str(4) == b"invalid cu_seqlens"
 
@@ -131,6 +132,23 @@ def test_merge_accum_cast_validation(L):
     assert L.attn_cast_bf16(4, None, P, None) == NULL
     assert L.attn_cast_bf16(4, P, None, None) == NULL
     assert L.attn_cast_bf16(0, None, None, None) == OK
+
+
+def test_gqa_validation(L):
+    def fwd(H=8, Hk=2, B=1, S=8):
+        return L.attn_fwd_gqa(B, S, S, H, Hk, 64, 0.125, P, P, P, None, P, P, None)
+
+    def bwd(H=8, Hk=2, B=1, S=8):
+        return L.attn_bwd_gqa(B, S, S, H, Hk, 64, 0.125, P, P, P, None, P, P, P, P, P, P, None)
+
+    for f in (fwd, bwd):
+        assert f(Hk=3) == SHAPE   # must divide H
+        assert f(Hk=0) == SHAPE
+        assert f(Hk=-2) == SHAPE
+        assert f(Hk=16) == SHAPE  # more key/value heads than query heads
+        assert f(H=0, Hk=0) == OK
+        assert f(B=0) == OK
+    assert L.attn_fwd_gqa(1, 8, 8, 8, 2, 64, 0.125, P, None, P, None, P, P, None) == NULL
 
 
 def _cu(vals):
