@@ -32,18 +32,23 @@ def _load():
     lib = ctypes.CDLL(_build.LIB)
     i, d = ctypes.c_int, ctypes.c_double
     lib.oracle_attn_fwd.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp]
+    lib.oracle_attn_fwd_ex.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp, i]
     lib.oracle_attn_delta.argtypes = [i, i, i, i, _dp, _dp, _dp]
     lib.oracle_attn_bwd.argtypes = [i, i, i, i, i, d, _dp, _dp, _dp, _u8p, _dp, _dp, _dp, _dp,
                                     _dp, _dp, _dp]
+    lib.oracle_attn_bwd_ex.argtypes = lib.oracle_attn_bwd.argtypes + [i]
     lib.oracle_set_num_threads.argtypes = [i]
     lib.oracle_attn_lse_merge.argtypes = [i, i, i, i, i, ctypes.POINTER(_dp), ctypes.POINTER(_dp),
                                           _dp, _dp]
     lib.oracle_attn_varlen_fwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp]
+    lib.oracle_attn_varlen_fwd_ex.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp, i]
     lib.oracle_attn_varlen_bwd.argtypes = [i, _i32p, i, i, d, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                            _dp, _dp, _dp]
+    lib.oracle_attn_varlen_bwd_ex.argtypes = lib.oracle_attn_varlen_bwd.argtypes + [i]
     for f in ("oracle_attn_fwd", "oracle_attn_delta", "oracle_attn_bwd", "oracle_attn_varlen_fwd",
               "oracle_attn_varlen_bwd", "oracle_num_threads", "oracle_set_num_threads",
-              "oracle_attn_lse_merge"):
+              "oracle_attn_lse_merge", "oracle_attn_fwd_ex", "oracle_attn_bwd_ex",
+              "oracle_attn_varlen_fwd_ex", "oracle_attn_varlen_bwd_ex"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -78,8 +83,9 @@ def _check(rc):
         raise ValueError(f"oracle rejected arguments (code {rc})")
 
 
-def attn_fwd(q, k, v, key_mask=None, scale=None):
-    """q (B,Sq,H,D), k/v (B,Sk,H,D) -> out (B,Sq,H,D), lse (B,H,Sq)."""
+def attn_fwd(q, k, v, key_mask=None, scale=None, causal=False):
+    """q (B,Sq,H,D), k/v (B,Sk,H,D) -> out (B,Sq,H,D), lse (B,H,Sq); causal: query i sees
+    keys j <= i only."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
@@ -90,9 +96,9 @@ def attn_fwd(q, k, v, key_mask=None, scale=None):
         assert mask.shape == (B, Sk)
     out = np.empty_like(q)
     lse = np.empty((B, H, Sq), dtype=np.float64)
-    _check(_load().oracle_attn_fwd(B, Sq, Sk, H, D, scale, _p(q), _p(k), _p(v),
-                                   None if mask is None else mask.ctypes.data_as(_u8p), _p(out),
-                                   _p(lse)))
+    _check(_load().oracle_attn_fwd_ex(B, Sq, Sk, H, D, scale, _p(q), _p(k), _p(v),
+                                      None if mask is None else mask.ctypes.data_as(_u8p), _p(out),
+                                      _p(lse), int(causal)))
     return out, lse
 
 
@@ -105,7 +111,8 @@ def attn_delta(out, dout):
     return delta
 
 
-def attn_bwd(q, k, v, out, lse, dout, key_mask=None, scale=None, want_dq=True, want_dkdv=True):
+def attn_bwd(q, k, v, out, lse, dout, key_mask=None, scale=None, want_dq=True, want_dkdv=True,
+             causal=False):
     """Return (delta, dq, dk, dv); dq or dk/dv are None when not requested.
 
     ``out`` and ``lse`` must come from :func:`attn_fwd` on the same inputs (or,
@@ -120,13 +127,14 @@ def attn_bwd(q, k, v, out, lse, dout, key_mask=None, scale=None, want_dq=True, w
     dq = np.empty_like(q) if want_dq else None
     dk = np.empty_like(k) if want_dkdv else None
     dv = np.empty_like(v) if want_dkdv else None
-    _check(_load().oracle_attn_bwd(B, Sq, Sk, H, D, scale, _p(q), _p(k), _p(v),
-                                   None if mask is None else mask.ctypes.data_as(_u8p), _p(out),
-                                   _p(lse), _p(dout), _p(delta), _p(dq), _p(dk), _p(dv)))
+    _check(_load().oracle_attn_bwd_ex(B, Sq, Sk, H, D, scale, _p(q), _p(k), _p(v),
+                                      None if mask is None else mask.ctypes.data_as(_u8p), _p(out),
+                                      _p(lse), _p(dout), _p(delta), _p(dq), _p(dk), _p(dv),
+                                      int(causal)))
     return delta, dq, dk, dv
 
 
-def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None):
+def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, causal=False):
     """Packed q/k/v (T,H,D) (a leading batch dim of 1 is accepted) -> out (T,H,D), lse (H,T)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     shp = q.shape
@@ -136,12 +144,12 @@ def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None):
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     out = np.empty_like(q)
     lse = np.empty((H, T), dtype=np.float64)
-    _check(_load().oracle_attn_varlen_fwd(len(cu) - 1, cu.ctypes.data_as(_i32p), H, D, scale,
-                                          _p(q), _p(k), _p(v), _p(out), _p(lse)))
+    _check(_load().oracle_attn_varlen_fwd_ex(len(cu) - 1, cu.ctypes.data_as(_i32p), H, D, scale,
+                                             _p(q), _p(k), _p(v), _p(out), _p(lse), int(causal)))
     return out, lse
 
 
-def attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None):
+def attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None, causal=False):
     """-> (delta (H,T), dq, dk, dv) for packed inputs."""
     q, k, v, out, lse, dout = map(_f64, (q, k, v, out, lse, dout))
     T, H, D = q.shape[-3:]
@@ -149,9 +157,9 @@ def attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None):
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     delta = np.empty((H, T), dtype=np.float64)
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
-    _check(_load().oracle_attn_varlen_bwd(len(cu) - 1, cu.ctypes.data_as(_i32p), H, D, scale,
-                                          _p(q), _p(k), _p(v), _p(out), _p(lse), _p(dout),
-                                          _p(delta), _p(dq), _p(dk), _p(dv)))
+    _check(_load().oracle_attn_varlen_bwd_ex(len(cu) - 1, cu.ctypes.data_as(_i32p), H, D, scale,
+                                             _p(q), _p(k), _p(v), _p(out), _p(lse), _p(dout),
+                                             _p(delta), _p(dq), _p(dk), _p(dv), int(causal)))
     return delta, dq, dk, dv
 
 
@@ -188,17 +196,18 @@ def _gqa_group(H, Hk):
     return H // Hk
 
 
-def attn_fwd_gqa(q, k, v, key_mask=None, scale=None):
+def attn_fwd_gqa(q, k, v, key_mask=None, scale=None, causal=False):
     """q (B,Sq,H,D), k/v (B,Sk,Hk,D) -> out (B,Sq,H,D), lse (B,H,Sq)."""
     G = _gqa_group(q.shape[2], k.shape[2])
-    return attn_fwd(q, np.repeat(_f64(k), G, axis=2), np.repeat(_f64(v), G, axis=2), key_mask, scale)
+    return attn_fwd(q, np.repeat(_f64(k), G, axis=2), np.repeat(_f64(v), G, axis=2), key_mask, scale,
+                    causal)
 
 
-def attn_bwd_gqa(q, k, v, out, lse, dout, key_mask=None, scale=None):
+def attn_bwd_gqa(q, k, v, out, lse, dout, key_mask=None, scale=None, causal=False):
     """-> (delta, dq (B,Sq,H,D), dk, dv (B,Sk,Hk,D))."""
     B, Sk, Hk, D = k.shape
     G = _gqa_group(q.shape[2], Hk)
     delta, dq, dke, dve = attn_bwd(q, np.repeat(_f64(k), G, axis=2), np.repeat(_f64(v), G, axis=2),
-                                   out, lse, dout, key_mask, scale)
+                                   out, lse, dout, key_mask, scale, causal=causal)
     return (delta, dq, dke.reshape(B, Sk, Hk, G, D).sum(axis=3),
             dve.reshape(B, Sk, Hk, G, D).sum(axis=3))

@@ -21,6 +21,10 @@
  *   dV_j   = sum_i P_ij dO_i
  *
  * LSE is an auxiliary, non-differentiable output (diffusers PR #14834 summary).
+ * Causal (the _ex entry points, causal = 1; named as not extended in diffusers PR
+ * #14834, description, and defined on no page): query row i attends to keys j <= i only,
+ * top-left aligned when Sq != Sk (the convention of torch's scaled_dot_product_attention
+ * with is_causal); in varlen mode within each sequence.  It combines with the key mask.
  * A boolean key mask becomes a 0 / -inf bias (diffusers PR #14341, follow-up 2);
  * here excluded keys are simply skipped.  The mask is head-broadcast, shape
  * (B, 1, 1, Sk) passed as (B, Sk) bytes, nonzero = attend (diffusers PR #14834,
@@ -56,16 +60,21 @@ typedef struct {
   int nq, nk, D;
   const uint8_t* mask; /* nk bytes or NULL */
   double scale;
+  int causal; /* query i sees keys j <= i only */
 } slice_t;
 
 static int key_on(const slice_t* s, int j) { return s->mask == NULL || s->mask[j] != 0; }
+/* Whether query row i attends to key j: the key mask and, when causal, j <= i. */
+static int pair_on(const slice_t* s, int i, int j) {
+  return key_on(s, j) && (!s->causal || j <= i);
+}
 
 /* Forward for query row i of the slice.  sbuf holds nk doubles. */
 static void fwd_row(const slice_t* s, int i, double* sbuf, double* out_i, double* lse_i) {
   const double* qi = s->q + (long)i * s->rs;
   double m = -INFINITY;
   for (int j = 0; j < s->nk; ++j) {
-    if (!key_on(s, j)) continue;
+    if (!pair_on(s, i, j)) continue;
     sbuf[j] = s->scale * dot(qi, s->k + (long)j * s->rs, s->D);
     if (sbuf[j] > m) m = sbuf[j];
   }
@@ -76,10 +85,10 @@ static void fwd_row(const slice_t* s, int i, double* sbuf, double* out_i, double
   }
   double l = 0.0;
   for (int j = 0; j < s->nk; ++j)
-    if (key_on(s, j)) l += exp(sbuf[j] - m);
+    if (pair_on(s, i, j)) l += exp(sbuf[j] - m);
   const double lse = m + log(l);
   for (int j = 0; j < s->nk; ++j) {
-    if (!key_on(s, j)) continue;
+    if (!pair_on(s, i, j)) continue;
     const double p = exp(sbuf[j] - lse);
     const double* vj = s->v + (long)j * s->rs;
     for (int d = 0; d < s->D; ++d) out_i[d] += p * vj[d];
@@ -95,7 +104,7 @@ static void dq_row(const slice_t* s, const double* dout, int i, double lse_i, do
   const double* qi = s->q + (long)i * s->rs;
   const double* doi = dout + (long)i * s->rs;
   for (int j = 0; j < s->nk; ++j) {
-    if (!key_on(s, j)) continue;
+    if (!pair_on(s, i, j)) continue;
     const double* kj = s->k + (long)j * s->rs;
     const double p = exp(s->scale * dot(qi, kj, s->D) - lse_i);
     const double dp = dot(doi, s->v + (long)j * s->rs, s->D);
@@ -112,7 +121,7 @@ static void dkdv_col(const slice_t* s, const double* dout, int j, const double* 
   const double* kj = s->k + (long)j * s->rs;
   const double* vj = s->v + (long)j * s->rs;
   for (int i = 0; i < s->nq; ++i) {
-    if (lse[i] == -INFINITY) continue;
+    if (lse[i] == -INFINITY || !pair_on(s, i, j)) continue;
     const double* qi = s->q + (long)i * s->rs;
     const double* doi = dout + (long)i * s->rs;
     const double p = exp(s->scale * dot(qi, kj, s->D) - lse[i]);
@@ -139,9 +148,9 @@ int oracle_set_num_threads(int n) {
 
 /* ---------------------------------------------------------------- dense BSHD */
 
-int oracle_attn_fwd(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
+int oracle_attn_fwd_ex(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
                     const double* k, const double* v, const uint8_t* key_mask, double* out,
-                    double* lse) {
+                    double* lse, int causal) {
   if (!check_dims(B, Sq, Sk, H, D)) return 2;
   const long rs = (long)H * D;
 #pragma omp parallel
@@ -153,13 +162,19 @@ int oracle_attn_fwd(int B, int Sq, int Sk, int H, int D, double scale, const dou
         for (int i = 0; i < Sq; ++i) {
           slice_t s = {q + (long)b * Sq * rs + (long)h * D, k + (long)b * Sk * rs + (long)h * D,
                        v + (long)b * Sk * rs + (long)h * D, rs, Sq, Sk, D,
-                       key_mask ? key_mask + (long)b * Sk : NULL, scale};
+                       key_mask ? key_mask + (long)b * Sk : NULL, scale, causal};
           fwd_row(&s, i, sbuf, out + ((long)b * Sq + i) * rs + (long)h * D,
                   lse + ((long)b * H + h) * Sq + i);
         }
     free(sbuf);
   }
   return 0;
+}
+
+int oracle_attn_fwd(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
+                    const double* k, const double* v, const uint8_t* key_mask, double* out,
+                    double* lse) {
+  return oracle_attn_fwd_ex(B, Sq, Sk, H, D, scale, q, k, v, key_mask, out, lse, 0);
 }
 
 int oracle_attn_delta(int B, int S, int H, int D, const double* out, const double* dout,
@@ -179,10 +194,10 @@ int oracle_attn_delta(int B, int S, int H, int D, const double* out, const doubl
 /* Backward.  out and lse are the forward's results; delta is formed from out
  * and written to delta_out when that is non-NULL.  Any of dq, dk, dv may be
  * NULL to skip that pass (dk and dv go together). */
-int oracle_attn_bwd(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
+int oracle_attn_bwd_ex(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
                     const double* k, const double* v, const uint8_t* key_mask, const double* out,
                     const double* lse, const double* dout, double* delta_out, double* dq,
-                    double* dk, double* dv) {
+                    double* dk, double* dv, int causal) {
   if (!check_dims(B, Sq, Sk, H, D)) return 2;
   if ((dk == NULL) != (dv == NULL)) return 1;
   const long rs = (long)H * D;
@@ -195,7 +210,7 @@ int oracle_attn_bwd(int B, int Sq, int Sk, int H, int D, double scale, const dou
         for (int i = 0; i < Sq; ++i) {
           slice_t s = {q + (long)b * Sq * rs + (long)h * D, k + (long)b * Sk * rs + (long)h * D,
                        v + (long)b * Sk * rs + (long)h * D, rs, Sq, Sk, D,
-                       key_mask ? key_mask + (long)b * Sk : NULL, scale};
+                       key_mask ? key_mask + (long)b * Sk : NULL, scale, causal};
           const long r = ((long)b * H + h) * Sq + i;
           dq_row(&s, dout + (long)b * Sq * rs + (long)h * D, i, lse[r], delta[r],
                  dq + ((long)b * Sq + i) * rs + (long)h * D);
@@ -208,7 +223,7 @@ int oracle_attn_bwd(int B, int Sq, int Sk, int H, int D, double scale, const dou
         for (int j = 0; j < Sk; ++j) {
           slice_t s = {q + (long)b * Sq * rs + (long)h * D, k + (long)b * Sk * rs + (long)h * D,
                        v + (long)b * Sk * rs + (long)h * D, rs, Sq, Sk, D,
-                       key_mask ? key_mask + (long)b * Sk : NULL, scale};
+                       key_mask ? key_mask + (long)b * Sk : NULL, scale, causal};
           const long r0 = ((long)b * H + h) * Sq;
           const long o = ((long)b * Sk + j) * rs + (long)h * D;
           dkdv_col(&s, dout + (long)b * Sq * rs + (long)h * D, j, lse + r0, delta + r0, dk + o,
@@ -217,6 +232,13 @@ int oracle_attn_bwd(int B, int Sq, int Sk, int H, int D, double scale, const dou
   }
   if (!delta_out) free(delta);
   return 0;
+}
+
+int oracle_attn_bwd(int B, int Sq, int Sk, int H, int D, double scale, const double* q,
+                    const double* k, const double* v, const uint8_t* key_mask, const double* out,
+                    const double* lse, const double* dout, double* delta_out, double* dq,
+                    double* dk, double* dv) {
+  return oracle_attn_bwd_ex(B, Sq, Sk, H, D, scale, q, k, v, key_mask, out, lse, dout, delta_out, dq, dk, dv, 0);
 }
 
 /* ------------------------------------------------------------ packed varlen */
@@ -230,9 +252,9 @@ static int check_cu(int nseq, const int32_t* cu) {
 
 /* Sequence n covers packed rows [cu[n], cu[n+1]); queries attend only to keys
  * of their own sequence (block-diagonal).  LSE is (H, T). */
-int oracle_attn_varlen_fwd(int nseq, const int32_t* cu, int H, int D, double scale,
+int oracle_attn_varlen_fwd_ex(int nseq, const int32_t* cu, int H, int D, double scale,
                            const double* q, const double* k, const double* v, double* out,
-                           double* lse) {
+                           double* lse, int causal) {
   if (!check_cu(nseq, cu) || H < 0 || D <= 0) return 4;
   const long rs = (long)H * D;
   const int T = cu[nseq];
@@ -249,7 +271,7 @@ int oracle_attn_varlen_fwd(int nseq, const int32_t* cu, int H, int D, double sca
         while (cu[n + 1] <= t) ++n;
         const int s0 = cu[n], L = cu[n + 1] - cu[n];
         slice_t s = {q + (long)s0 * rs + (long)h * D, k + (long)s0 * rs + (long)h * D,
-                     v + (long)s0 * rs + (long)h * D, rs, L, L, D, NULL, scale};
+                     v + (long)s0 * rs + (long)h * D, rs, L, L, D, NULL, scale, causal};
         fwd_row(&s, t - s0, sbuf, out + (long)t * rs + (long)h * D, lse + (long)h * T + t);
       }
     free(sbuf);
@@ -257,10 +279,16 @@ int oracle_attn_varlen_fwd(int nseq, const int32_t* cu, int H, int D, double sca
   return 0;
 }
 
-int oracle_attn_varlen_bwd(int nseq, const int32_t* cu, int H, int D, double scale,
+int oracle_attn_varlen_fwd(int nseq, const int32_t* cu, int H, int D, double scale,
+                           const double* q, const double* k, const double* v, double* out,
+                           double* lse) {
+  return oracle_attn_varlen_fwd_ex(nseq, cu, H, D, scale, q, k, v, out, lse, 0);
+}
+
+int oracle_attn_varlen_bwd_ex(int nseq, const int32_t* cu, int H, int D, double scale,
                            const double* q, const double* k, const double* v, const double* out,
                            const double* lse, const double* dout, double* delta_out, double* dq,
-                           double* dk, double* dv) {
+                           double* dk, double* dv, int causal) {
   if (!check_cu(nseq, cu) || H < 0 || D <= 0) return 4;
   if ((dk == NULL) != (dv == NULL)) return 1;
   const long rs = (long)H * D;
@@ -275,7 +303,7 @@ int oracle_attn_varlen_bwd(int nseq, const int32_t* cu, int H, int D, double sca
       while (cu[n + 1] <= t) ++n;
       const int s0 = cu[n], L = cu[n + 1] - cu[n];
       slice_t s = {q + (long)s0 * rs + (long)h * D, k + (long)s0 * rs + (long)h * D,
-                   v + (long)s0 * rs + (long)h * D, rs, L, L, D, NULL, scale};
+                   v + (long)s0 * rs + (long)h * D, rs, L, L, D, NULL, scale, causal};
       const long r0 = (long)h * T + s0;
       if (dq)
         dq_row(&s, dout + (long)s0 * rs + (long)h * D, t - s0, lse[r0 + t - s0],
@@ -286,6 +314,13 @@ int oracle_attn_varlen_bwd(int nseq, const int32_t* cu, int H, int D, double sca
     }
   if (!delta_out) free(delta);
   return 0;
+}
+
+int oracle_attn_varlen_bwd(int nseq, const int32_t* cu, int H, int D, double scale,
+                           const double* q, const double* k, const double* v, const double* out,
+                           const double* lse, const double* dout, double* delta_out, double* dq,
+                           double* dk, double* dv) {
+  return oracle_attn_varlen_bwd_ex(nseq, cu, H, D, scale, q, k, v, out, lse, dout, delta_out, dq, dk, dv, 0);
 }
 
 /* ---------------------------------------------------------------- chunk merge */
