@@ -54,12 +54,17 @@ def lib():
     L.attn_varlen_bwd.argtypes = [i, vp, vp, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_lse_merge.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp]
     L.attn_fwd_gqa.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_fwd_ex.argtypes = [i, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_bwd_ex.argtypes = [i, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_varlen_fwd_ex.argtypes = [i, vp, vp, i, i, f, i, vp, vp, vp, vp, vp, vp]
+    L.attn_varlen_bwd_ex.argtypes = [i, vp, vp, i, i, f, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_bwd_gqa.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_bwd_accum.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.attn_cast_bf16.argtypes = [ctypes.c_int64, vp, vp, vp]
     for name in ("attn_abi_version", "attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                  "attn_varlen_fwd", "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum",
-                 "attn_cast_bf16", "attn_fwd_gqa", "attn_bwd_gqa"):
+                 "attn_cast_bf16", "attn_fwd_gqa", "attn_bwd_gqa", "attn_fwd_ex", "attn_bwd_ex",
+                 "attn_varlen_fwd_ex", "attn_varlen_bwd_ex"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -135,10 +140,13 @@ def _kv_heads(q, k):
     return Hk
 
 
-def attn_fwd(q, k, v, key_mask=None, scale=None, out=None, lse=None):
+CAUSAL = 1
+
+
+def attn_fwd(q, k, v, key_mask=None, scale=None, out=None, lse=None, causal=False):
     """out, lse = attn_fwd(q, k, v): q (B,Sq,H,D), k/v (B,Sk,Hk,D) bf16 (Hk dividing H:
     grouped-query attention, query head h reading key/value head h // (H/Hk))
-    -> out bf16, lse fp32 (B,H,Sq)."""
+    -> out bf16, lse fp32 (B,H,Sq).  causal: query i sees keys j <= i only."""
     torch = _torch()
     B, Sq, Sk, H, D = _dims(q, k)
     Hk = _kv_heads(q, k)
@@ -153,8 +161,9 @@ def attn_fwd(q, k, v, key_mask=None, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     _want(out, "out", (B, Sq, H, D), torch.bfloat16)
     _want(lse, "lse", (B, H, Sq), torch.float32)
-    _check("attn_fwd", lib().attn_fwd_gqa(B, Sq, Sk, H, Hk, D, scale, _ptr(q), _ptr(k), _ptr(v),
-                                          _ptr(m), _ptr(out), _ptr(lse), _stream()))
+    _check("attn_fwd", lib().attn_fwd_ex(B, Sq, Sk, H, Hk, D, scale, CAUSAL if causal else 0,
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(out),
+                                         _ptr(lse), _stream()))
     return out, lse
 
 
@@ -174,7 +183,8 @@ def attn_bwd_preprocess(out, dout, delta=None):
     return delta
 
 
-def attn_bwd(q, k, v, lse, delta, dout, key_mask=None, scale=None, dq=None, dk=None, dv=None):
+def attn_bwd(q, k, v, lse, delta, dout, key_mask=None, scale=None, dq=None, dk=None, dv=None,
+             causal=False):
     """dq, dk, dv = attn_bwd(q, k, v, lse, delta, dout) (bf16 BSHD grads; dk, dv have k's
     Hk heads, each summing its query heads' contributions)."""
     torch = _torch()
@@ -194,9 +204,10 @@ def attn_bwd(q, k, v, lse, delta, dout, key_mask=None, scale=None, dq=None, dk=N
     _want(dq, "dq", (B, Sq, H, D), torch.bfloat16)
     _want(dk, "dk", (B, Sk, Hk, D), torch.bfloat16)
     _want(dv, "dv", (B, Sk, Hk, D), torch.bfloat16)
-    _check("attn_bwd", lib().attn_bwd_gqa(B, Sq, Sk, H, Hk, D, scale, _ptr(q), _ptr(k), _ptr(v),
-                                          _ptr(m), _ptr(lse), _ptr(delta), _ptr(dout), _ptr(dq),
-                                          _ptr(dk), _ptr(dv), _stream()))
+    _check("attn_bwd", lib().attn_bwd_ex(B, Sq, Sk, H, Hk, D, scale, CAUSAL if causal else 0,
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(lse),
+                                         _ptr(delta), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                         _stream()))
     return dq, dk, dv
 
 
@@ -230,7 +241,7 @@ def _thd(x, name):
     return x
 
 
-def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None):
+def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None, causal=False):
     """Packed varlen forward: q/k/v (T,H,D) bf16, cu_seqlens int32[nseq+1] -> out (T,H,D), lse (H,T)."""
     torch = _torch()
     q3, k3, v3 = _thd(q, "q"), _thd(k, "k"), _thd(v, "v")
@@ -246,13 +257,15 @@ def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None):
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _want(_thd(out, "out"), "out", (T, H, D), torch.bfloat16)
     _want(lse, "lse", (H, T), torch.float32)
-    _check("attn_varlen_fwd", lib().attn_varlen_fwd(nseq, _ptr(host), _ptr(dev), H, D, scale,
-                                                    _ptr(q3), _ptr(k3), _ptr(v3), _ptr(out),
-                                                    _ptr(lse), _stream()))
+    _check("attn_varlen_fwd", lib().attn_varlen_fwd_ex(nseq, _ptr(host), _ptr(dev), H, D, scale,
+                                                       CAUSAL if causal else 0, _ptr(q3),
+                                                       _ptr(k3), _ptr(v3), _ptr(out), _ptr(lse),
+                                                       _stream()))
     return out, lse
 
 
-def attn_varlen_bwd(q, k, v, lse, delta, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None):
+def attn_varlen_bwd(q, k, v, lse, delta, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None,
+                    causal=False):
     """Packed varlen backward -> dq, dk, dv (T,H,D).  delta = attn_bwd_preprocess(out, dout)[0]."""
     torch = _torch()
     q3, k3, v3, o3 = _thd(q, "q"), _thd(k, "k"), _thd(v, "v"), _thd(dout, "dout")
@@ -273,10 +286,11 @@ def attn_varlen_bwd(q, k, v, lse, delta, dout, cu_seqlens, scale=None, dq=None, 
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _want(_thd(t, n), n, (T, H, D), torch.bfloat16)
-    _check("attn_varlen_bwd", lib().attn_varlen_bwd(nseq, _ptr(host), _ptr(dev), H, D, scale,
-                                                    _ptr(q3), _ptr(k3), _ptr(v3), _ptr(lse),
-                                                    _ptr(delta), _ptr(o3), _ptr(dq), _ptr(dk),
-                                                    _ptr(dv), _stream()))
+    _check("attn_varlen_bwd", lib().attn_varlen_bwd_ex(nseq, _ptr(host), _ptr(dev), H, D, scale,
+                                                       CAUSAL if causal else 0, _ptr(q3),
+                                                       _ptr(k3), _ptr(v3), _ptr(lse), _ptr(delta),
+                                                       _ptr(o3), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                       _stream()))
     return dq, dk, dv
 
 

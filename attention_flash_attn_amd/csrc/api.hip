@@ -15,7 +15,7 @@ using attn::FwdParams;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
 // The backward starts its score accumulators from -LSE/scale; the lower bound keeps that
@@ -84,14 +84,21 @@ int attn_abi_version(void) { return kAbiVersion; }
 
 int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, void* out, float* lse, void* stream) {
-  return attn_fwd_gqa(B, Sq, Sk, H, H, D, scale, q, k, v, key_mask, out, lse, stream);
+  return attn_fwd_ex(B, Sq, Sk, H, H, D, scale, 0, q, k, v, key_mask, out, lse, stream);
 }
 
 int attn_fwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
                  const void* k, const void* v, const uint8_t* key_mask, void* out, float* lse,
                  void* stream) {
+  return attn_fwd_ex(B, Sq, Sk, H, Hk, D, scale, 0, q, k, v, key_mask, out, lse, stream);
+}
+
+int attn_fwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int flags,
+                const void* q, const void* k, const void* v, const uint8_t* key_mask, void* out,
+                float* lse, void* stream) {
   int st = check_dense(B, Sq, Sk, H, D, scale);
   if (st == ATTN_OK) st = check_kv_heads(H, Hk);
+  if (st == ATTN_OK && (flags & ~ATTN_CAUSAL)) st = ATTN_ERR_SHAPE;
   if (st != ATTN_OK) return st;
   const bool has_q = (long)B * Sq * H > 0, has_k = (long)B * Sk * Hk > 0;
   if (missing(q, has_q) || missing(out, has_q) || missing(lse, has_q) || missing(k, has_k) ||
@@ -112,6 +119,7 @@ int attn_fwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const
   p.H = H;
   p.Hk = Hk;
   p.G = H / Hk;
+  p.causal = flags & ATTN_CAUSAL;
   p.n_qtiles = (int)cdiv(Sq, attn::kFwdBlockM);
   p.n_blocks = p.n_qtiles * H * B;
   p.c2 = scale * attn::kLog2e;
@@ -172,16 +180,25 @@ static void bwd_grid(BwdParams& p, int nq, int nk, int outer) {
 int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, const float* lse, const float* delta,
              const void* dout, void* dq, void* dk, void* dv, void* stream) {
-  return attn_bwd_gqa(B, Sq, Sk, H, H, D, scale, q, k, v, key_mask, lse, delta, dout, dq, dk, dv,
-                      stream);
+  return attn_bwd_ex(B, Sq, Sk, H, H, D, scale, 0, q, k, v, key_mask, lse, delta, dout, dq, dk,
+                     dv, stream);
 }
 
 int attn_bwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
                  const void* k, const void* v, const uint8_t* key_mask, const float* lse,
                  const float* delta, const void* dout, void* dq, void* dk, void* dv,
                  void* stream) {
+  return attn_bwd_ex(B, Sq, Sk, H, Hk, D, scale, 0, q, k, v, key_mask, lse, delta, dout, dq, dk,
+                     dv, stream);
+}
+
+int attn_bwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int flags,
+                const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                const float* lse, const float* delta, const void* dout, void* dq, void* dk,
+                void* dv, void* stream) {
   int st = check_dense(B, Sq, Sk, H, D, scale);
   if (st == ATTN_OK) st = check_kv_heads(H, Hk);
+  if (st == ATTN_OK && (flags & ~ATTN_CAUSAL)) st = ATTN_ERR_SHAPE;
   if (st != ATTN_OK) return st;
   const bool hq = (long)B * Sq * H > 0, hk = (long)B * Sk * Hk > 0;
   if (missing(q, hq) || missing(lse, hq) || missing(delta, hq) || missing(dout, hq) ||
@@ -191,6 +208,7 @@ int attn_bwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   BwdParams p = bwd_params(B, Sq, Sk, H, Hk, scale, q, k, v, key_mask, lse, delta, dout, dq, dk,
                            dv, nullptr);
+  p.causal = flags & ATTN_CAUSAL;
   bwd_grid(p, Sq, Sk, B);
   return status_of(attn::launch_bwd(D, false, false, p, s));
 }
@@ -255,7 +273,15 @@ int attn_cast_bf16(int64_t n, const float* src, void* dst, void* stream) {
 int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
                     int H, int D, float scale, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* stream) {
+  return attn_varlen_fwd_ex(nseq, cu_seqlens_host, cu_seqlens_dev, H, D, scale, 0, q, k, v, out,
+                            lse, stream);
+}
+
+int attn_varlen_fwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                       int H, int D, float scale, int flags, const void* q, const void* k,
+                       const void* v, void* out, float* lse, void* stream) {
   if (!cu_seqlens_host || !cu_seqlens_dev) return ATTN_ERR_NULL;
+  if (flags & ~ATTN_CAUSAL) return ATTN_ERR_SHAPE;
   int T = 0, maxlen = 0;
   const int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
   if (st != ATTN_OK) return st;
@@ -276,6 +302,7 @@ int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
   p.H = H;
   p.Hk = H;
   p.G = 1;
+  p.causal = flags & ATTN_CAUSAL;
   p.n_qtiles = (int)cdiv(maxlen, attn::kFwdBlockM);
   p.n_blocks = p.n_qtiles * H * nseq;
   p.c2 = scale * attn::kLog2e;
@@ -286,7 +313,16 @@ int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
                     int H, int D, float scale, const void* q, const void* k, const void* v,
                     const float* lse, const float* delta, const void* dout, void* dq, void* dk,
                     void* dv, void* stream) {
+  return attn_varlen_bwd_ex(nseq, cu_seqlens_host, cu_seqlens_dev, H, D, scale, 0, q, k, v, lse,
+                            delta, dout, dq, dk, dv, stream);
+}
+
+int attn_varlen_bwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                       int H, int D, float scale, int flags, const void* q, const void* k,
+                       const void* v, const float* lse, const float* delta, const void* dout,
+                       void* dq, void* dk, void* dv, void* stream) {
   if (!cu_seqlens_host || !cu_seqlens_dev) return ATTN_ERR_NULL;
+  if (flags & ~ATTN_CAUSAL) return ATTN_ERR_SHAPE;
   int T = 0, maxlen = 0;
   const int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
   if (st != ATTN_OK) return st;
@@ -299,6 +335,7 @@ int attn_varlen_bwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
   hipStream_t s = static_cast<hipStream_t>(stream);
   BwdParams p = bwd_params(nseq, T, T, H, H, scale, q, k, v, nullptr, lse, delta, dout, dq, dk,
                            dv, cu_seqlens_dev);
+  p.causal = flags & ATTN_CAUSAL;
   bwd_grid(p, maxlen, maxlen, nseq);
   return status_of(attn::launch_bwd(D, true, false, p, s));
 }

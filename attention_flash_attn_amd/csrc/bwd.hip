@@ -222,10 +222,15 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   // its asynchronous copy and only used when published after the current tile's
   // compute: a use right after the load would make the wave wait for the whole copy.
   float lraw = 0.f, draw = 0.f;
-  const int ntq = (nq + BQ - 1) / BQ;  // query tiles per query head
-  // Tile t of the loop: query head qhead + t / ntq, rows (t % ntq) * BQ ...
+  // Query tiles per query head: all of them, or (causal) those from the first one holding
+  // a row that sees key kb0.
+  const int ntq_all = (nq + BQ - 1) / BQ;
+  const int qt0 = p.causal ? min(kb0 / BQ, ntq_all) : 0;
+  const int ntq = ntq_all - qt0;
+  // Tile t of the loop: query head qhead + t / ntq, rows (qt0 + t % ntq) * BQ ...
+  auto tile_q0 = [&](int t) { return (qt0 + t - (t / ntq) * ntq) * BQ; };
   auto issue = [&](int t, char* qt, char* ot) {
-    const int i = t / ntq, q0 = (t - i * ntq) * BQ;
+    const int i = t / ntq, q0 = tile_q0(t);
     const long qi = sl.lse_base + (long)i * p.Sq + min(q0 + lane, nq - 1);
     lraw = p.lse[qi];
     draw = p.delta[qi];
@@ -238,12 +243,13 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     }
   };
   // Published per row: -LSE/scale and -delta, the starting values of the S and dP
-  // accumulators (rows past the end get -inf, so their P is 0).
+  // accumulators (rows past the end, and rows with no key to attend to, get -inf, so
+  // their P is 0).
   const float nis = -1.f / p.scale;
   auto publish_stats = [&](int t, float* lt, float* dt) {
-    const int q0 = (t - (t / ntq) * ntq) * BQ;
+    const int q0 = tile_q0(t);
     if (tid < BQ) {
-      const bool in = q0 + tid < nq;
+      const bool in = q0 + tid < nq && lraw != -INFINITY;
       lt[tid] = in ? lraw * nis : -INFINITY;
       dt[tid] = in ? -draw : 0.f;
     }
@@ -259,15 +265,23 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   // weights P = exp(scale S - LSE) and dS = P (dP - delta), then dV^T += dO^T P and
   // dK^T += Q^T dS.  The S and dP accumulators start from their rows' -LSE/scale and
   // -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in registers.
-  // No masking here: with one key per lane, P and dS of an excluded key only reach that
-  // key's own accumulators, which are stored as zeros.
+  // No key-mask work here: with one key per lane, P and dS of an excluded key only reach
+  // that key's own accumulators, which are stored as zeros.  Causal tiles on the diagonal
+  // zero P per element in a branch taken only there.
   auto compute = [&](const char* kt, const char* vt, const char* qt, const char* ot,
-                     const float* lt, const float* dt) {
+                     const float* lt, const float* dt, int q0) {
     // Register r holds query 32*sub + 16*(r/8) + 8*hl + r%8 of the tile.
     f32x16 s = row_values16(lt + 32 * sub + 8 * hl), dp = row_values16(dt + 32 * sub + 8 * hl);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       s = mfma32(lds_row16(qt, qr + qoff[ks]), lds_row16(kt, kr + qoff[ks]), s);
+    if (p.causal && q0 < kb0 + BN - 1) {
+      keep_branch();
+      // A tile on the diagonal: P = 0 where this lane's key comes after register r's row.
+      const int first = key - q0 - 32 * sub - 8 * hl;  // row offset below which P = 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 16 * (r >> 3) + (r & 7) >= first ? s[r] : -INFINITY;
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       dp = mfma32(lds_row16(ot, qr + qoff[ks]), lds_row16(vt, kr + qoff[ks]), dp);
@@ -297,7 +311,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
                   char* __restrict__ no_, float* __restrict__ nl, float* __restrict__ nd) {
     const bool more = j + 1 < ntiles;
     if (more) issue(j + 1, nq_, no_);
-    if (kball != 0) compute(kt, vt, cq, co, cl, cd);
+    if (kball != 0) compute(kt, vt, cq, co, cl, cd, tile_q0(j));
     if (more) publish_stats(j + 1, nl, nd);
     wait_tile_loads();
     __syncthreads();
@@ -372,7 +386,8 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int hl = lane >> 5, l32 = lane & 31;
-  const int qb = sl.tile * BM;
+  // Causal: the last query tiles see the most keys, so they are dealt out first.
+  const int qb = (p.causal ? p.n_q_tiles - 1 - sl.tile : sl.tile) * BM;
   if (qb >= sl.nq) return;  // block-uniform
   // Q/dO/dQ rows hold H heads, K/V rows Hk (this query head reads key/value head kvhead).
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
@@ -388,7 +403,10 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       doreg[ks] = as_bf16x8(ld16(p.dout + off + 16 * ks));
     }
   }
-  const float lse2 = qrow < nq ? p.lse[sl.lse_base + qrow] * kLog2e : INFINITY;
+  // Rows past the end, and rows with no key to attend to (LSE = -inf: every visible key
+  // masked), take +inf so that P = exp2(c2 S - lse2) is 0 even where S is -inf.
+  const float lse_row = qrow < nq ? p.lse[sl.lse_base + qrow] : -INFINITY;
+  const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
   const float dl = qrow < nq ? p.delta[sl.lse_base + qrow] : 0.f;
 
   // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
@@ -445,12 +463,20 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) dpt = mfma32(lds_row16(vt, rb + koff[ks]), doreg[ks], dpt);
   };
-  auto mask_scores = [&](uint64_t vw, int kb, f32x16& st) {
-    // register r's key is bit 32kb + 16(r/8) + 8hl + r%8 of vw
+  auto mask_scores = [&](uint64_t vw, int k0, int kb, f32x16& st) {
+    // register r's key is k0 + 32kb + 16(r/8) + 8hl + r%8 (bit 32kb + 16(r/8) + 8hl + r%8 of
+    // vw); causal: visible only up to this lane's query row
     const uint32_t w = (uint32_t)((vw >> (8 * hl)) >> (32 * kb));
+    const int last = p.causal ? qrow - k0 - 32 * kb - 8 * hl : BN;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] = (w >> (16 * (r >> 3) + (r & 7))) & 1u ? st[r] : -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const bool on = ((w >> (16 * (r >> 3) + (r & 7))) & 1u) && 16 * (r >> 3) + (r & 7) <= last;
+      st[r] = on ? st[r] : -INFINITY;
+    }
   };
+  // Tiles that need per-element masking: not every key valid, or (causal) some key of the
+  // tile after some query row of the workgroup.
+  auto needs_mask = [&](int k0, uint64_t vw) { return vw != ~0ull || (p.causal && k0 + BN - 1 > qb); };
   auto weights = [&](f32x16& st, f32x16& dpt, bf16x8 (&ds)[2]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -468,22 +494,23 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       dqacc[mb] = mfma32(lds_tr8(kt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds[1], dqacc[mb]);
     }
   };
-  auto compute = [&](const char* kt, const char* vt, uint64_t vw) {
+  auto compute = [&](const char* kt, const char* vt, int k0, uint64_t vw) {
     offsets();
     f32x16 st0, dpt0, st1, dpt1;
     bf16x8 ds0[2], ds1[2];
     scores(kt, vt, 0, st0, dpt0);
-    if (vw != ~0ull) {
+    const bool masked = needs_mask(k0, vw);
+    if (masked) {
       keep_branch();
-      mask_scores(vw, 0, st0);
+      mask_scores(vw, k0, 0, st0);
     }
     __builtin_amdgcn_sched_barrier(0);
     scores(kt, vt, 1, st1, dpt1);
     weights(st0, dpt0, ds0);
     __builtin_amdgcn_sched_barrier(0);
-    if (vw != ~0ull) {
+    if (masked) {
       keep_branch();
-      mask_scores(vw, 1, st1);
+      mask_scores(vw, k0, 1, st1);
     }
     grad(kt, 0, ds0);
     weights(st1, dpt1, ds1);
@@ -491,7 +518,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     grad(kt, 1, ds1);
   };
 
-  const int ntiles = (nk + BN - 1) / BN;
+  // Causal: keys past the workgroup's last query row are never seen.
+  const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
+  const int ntiles = (kend + BN - 1) / BN;
   uint64_t vw = 0;
   const KeyValidity kv{sl.mask, nk};
   uint32_t mbytes = 0;  // raw mask bytes of tile j + 1 during step j
@@ -505,7 +534,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
       issue((j + 1) * BN, nk_, nv);
     }
-    if (vw != 0) compute(ck, cv, vw);
+    if (vw != 0) compute(ck, cv, j * BN, vw);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int logical = xcd_remap(blockIdx.x, p.n_blocks);
-  const int qt = logical % p.n_qtiles;
+  // Causal: the last query tiles see the most keys, so they are dealt out first.
+  const int qt = p.causal ? p.n_qtiles - 1 - logical % p.n_qtiles : logical % p.n_qtiles;
   const int rest = logical / p.n_qtiles;
   // (outer, head) groups go head-major: each XCD's contiguous range of groups then holds
   // every batch|sequence of a few heads, so the ranges carry equal work even when the
@@ -116,7 +117,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = p.c2;
 
-  auto compute = [&](const char* kt, const char* vt, uint64_t vw) {
+  // Tiles that need per-element masking: not every key valid (mask, ragged tail), or, when
+  // causal, some key of the tile after some query row of the workgroup.
+  auto needs_mask = [&](int k0, uint64_t vw) { return vw != ~0ull || (p.causal && k0 + BN - 1 > qb); };
+  auto compute = [&](const char* kt, const char* vt, int k0, uint64_t vw) {
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -125,16 +129,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       for (int ks = 0; ks < NKS; ++ks)
         sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
     }
-    if (vw != ~0ull) {
+    if (needs_mask(k0, vw)) {
       keep_branch();
-      // Partial tile.  Bit (32kb + 16(r/8) + 8hl + r%8) of vw is register r's key.
+      // Register r of half kb holds key k0 + 32kb + 16(r/8) + 8hl + r%8 (its bit in vw is
+      // that minus k0) of this lane's query row qrow.
       const uint64_t vl = vw >> (8 * hl);
       const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
+      const int last = p.causal ? qrow - k0 - 8 * hl : BN;  // largest visible key - k0 - 8hl
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sacc[kb][r] = (w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u ? sacc[kb][r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int kr = 32 * kb + 16 * (r >> 3) + (r & 7);
+          const bool on = ((w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u) && kr <= last;
+          sacc[kb][r] = on ? sacc[kb][r] : -INFINITY;
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -178,7 +187,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         }
   };
 
-  const int ntiles = (nk + BN - 1) / BN;
+  // Causal: keys past the workgroup's last query row are never seen.
+  const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
+  const int ntiles = (kend + BN - 1) / BN;
   uint64_t vw = 0;
   const KeyValidity kv{mask, nk};
   uint32_t mbytes = 0;  // raw mask bytes of tile j + 1 during step j
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
       issue((j + 1) * BN, kn, vn);
     }
-    if (vw != 0) compute(kt, vt, vw);
+    if (vw != 0) compute(kt, vt, j * BN, vw);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;

@@ -17,6 +17,7 @@ struct FwdParams {
   const int32_t* cu;  // varlen only (device)
   int B, Sq, Sk, H;
   int Hk, G;     // key/value heads and query heads per key/value head (H = G * Hk)
+  int causal;    // query row i sees keys j <= i only (within its sequence)
   int n_qtiles;  // query tiles per (outer, head)
   int n_blocks;
   float c2;  // scale * log2(e)
@@ -40,6 +41,7 @@ struct BwdParams {
   const int32_t* cu;
   int B, Sq, Sk, H;
   int Hk, G;       // key/value heads and query heads per key/value head (H = G * Hk)
+  int causal;      // query row i sees keys j <= i only (within its sequence)
   int n_kv_tiles;  // dK/dV workgroups per (outer, key/value head)
   int n_q_tiles;   // dQ workgroups per (outer, query head)
   int dkdv_first;  // grid order inside a group: the longer workgroup kind first

@@ -64,6 +64,7 @@ class Workload:
     seqlens: Optional[Sequence[int]] = None  # varlen sequence lengths (packed)
     seed: int = 0
     Hk: Optional[int] = None  # key/value heads (grouped-query attention); None = H
+    causal: bool = False  # query i sees keys j <= i only
 
     @property
     def kv_heads(self) -> int:
@@ -103,10 +104,12 @@ class Workload:
         return m
 
     def fwd_flops(self) -> float:
-        """Algorithmic forward FLOPs: 4*H*D*sum(Sq*Sk) over (b | sequence); dense count for masks."""
+        """Algorithmic forward FLOPs: 4*H*D per (query, key) pair attended, over (b | sequence):
+        Sq*Sk pairs (dense count for masks), or S(S+1)/2 when causal."""
+        pairs = (lambda n: n * (n + 1) // 2) if self.causal else (lambda n: n * n)
         if self.varlen:
-            return 4.0 * self.H * self.D * float(sum(int(n) ** 2 for n in self.seqlens))
-        return 4.0 * self.B * self.H * self.S * self.S * self.D
+            return 4.0 * self.H * self.D * float(sum(pairs(int(n)) for n in self.seqlens))
+        return 4.0 * self.B * self.H * self.D * float(pairs(self.S))
 
     def fwd_bwd_flops(self) -> float:
         return 3.5 * self.fwd_flops()
@@ -122,6 +125,9 @@ WORKLOADS = {
     # Grouped-query attention (named as not yet extended in diffusers PR #14834, description;
     # the pages give no GQA workload): the Wan shard's query heads over 2 key/value heads.
     "wan_shard_gqa": Workload("wan_shard_gqa", B=1, S=27280, H=10, D=128, seed=6, Hk=2),
+    # Causal attention (also named as not yet extended there; the pages give no causal
+    # workload): the Wan shard's shape with query i seeing keys 0..i.
+    "wan_shard_causal": Workload("wan_shard_causal", B=1, S=27280, H=10, D=128, seed=7, causal=True),
 }
 
 

@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan_shard",
                     help="wan_shard (the metric's workload) or another named workload: "
-                         "probe_hs16, dit_s1024, mask_s4096, varlen4")
+                         "probe_hs16, dit_s1024, mask_s4096, varlen4, wan_shard_gqa, "
+                         "wan_shard_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=27280,
                     help="query rows of one head in the CPU-oracle sample")
@@ -87,10 +88,12 @@ def describe(w):
     if w.name == "wan_shard":
         return (f"wan_shard: B={w.B} N={w.S} H={w.H} D={w.D}, BSHD bf16, non-causal, no mask "
                 "(one Ulysses rank of the 40-head Wan layer)")
+    kind = "causal (FLOPs of the S(S+1)/2 attended pairs)" if w.causal else "non-causal"
     if w.varlen:
-        return f"{w.name}: packed varlen lengths {list(w.seqlens)} H={w.H} D={w.D}, bf16, non-causal"
+        return f"{w.name}: packed varlen lengths {list(w.seqlens)} H={w.H} D={w.D}, bf16, {kind}"
     m = f"key mask valid lengths {list(w.valid_lens)}" if w.valid_lens else "no mask"
-    return f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}, BSHD bf16, non-causal, {m}"
+    kv = f" Hk={w.Hk}" if w.Hk is not None else ""
+    return f"{w.name}: B={w.B} S={w.S} H={w.H}{kv} D={w.D}, BSHD bf16, {kind}, {m}"
 
 
 def cpu_model():
@@ -164,8 +167,8 @@ def run_ring(args, w, t, C):
 
     import attention_flash_attn_amd as A
 
-    if w.varlen:
-        raise SystemExit("--ring-chunks applies to dense workloads")
+    if w.varlen or w.causal or w.Hk is not None:
+        raise SystemExit("--ring-chunks applies to dense non-causal multi-head workloads")
     dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = (dev(x) for x in (t.q, t.k, t.v, t.do))
     B, S, H, D = w.B, w.S, w.H, w.D
@@ -276,18 +279,19 @@ def main():
         if ev is not None:
             ev[0].record()
         if w.varlen:
-            A.attn_varlen_fwd(q, k, v, (cu_host, cu_dev), None, out=out, lse=lse)
+            A.attn_varlen_fwd(q, k, v, (cu_host, cu_dev), None, out=out, lse=lse, causal=w.causal)
         else:
-            A.attn_fwd(q, k, v, mask, None, out=out, lse=lse)
+            A.attn_fwd(q, k, v, mask, None, out=out, lse=lse, causal=w.causal)
         if ev is not None:
             ev[1].record()
         A.attn_bwd_preprocess(out, do, delta=delta)
         if ev is not None:
             ev[2].record()
         if w.varlen:
-            A.attn_varlen_bwd(q, k, v, lse, delta, do, (cu_host, cu_dev), None, dq=dq, dk=dk, dv=dv)
+            A.attn_varlen_bwd(q, k, v, lse, delta, do, (cu_host, cu_dev), None, dq=dq, dk=dk, dv=dv,
+                              causal=w.causal)
         else:
-            A.attn_bwd(q, k, v, lse, delta, do, mask, None, dq=dq, dk=dk, dv=dv)
+            A.attn_bwd(q, k, v, lse, delta, do, mask, None, dq=dq, dk=dk, dv=dv, causal=w.causal)
         if ev is not None:
             ev[3].record()
 
@@ -333,7 +337,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: q,k,v,dO ~ N(0,1) seed 4, rounded to bf16",
+        "data": f"synthetic: q,k,v,dO ~ N(0,1) seed {w.seed}, rounded to bf16",
         "config": {"workload": describe(w), "batch": B, "seq_len": S, "heads": H,
                    "head_dim": D, "parallelism": "none"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -354,7 +358,7 @@ def main():
                      "traffic": recorded_traffic(w.name, dom)},
     }
     res.update(calibration_copy(args.copy_calibration_mb))
-    if not args.no_cpu_baseline and not w.varlen and w.valid_lens is None:
+    if not args.no_cpu_baseline and not w.varlen and w.valid_lens is None and not w.causal:
         res["cpu_baseline"] = cpu_baseline(w, t, min(args.cpu_rows, w.S))
     print(json.dumps(res), flush=True)
 

@@ -113,6 +113,23 @@ int attn_bwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const
                  void* stream);
 
 /*
+ * The general forms: Hk key/value heads as in attn_fwd_gqa / attn_bwd_gqa, and flags.
+ * ATTN_CAUSAL: query row i attends to keys j <= i only (top-left aligned when Sq != Sk,
+ * as torch's scaled_dot_product_attention with is_causal), combined with key_mask.  Causal
+ * attention is named as not yet extended in diffusers PR #14834 (description); the pages
+ * define no convention of their own.  Key tiles past a workgroup's last query row are
+ * skipped, so a causal call does about half the work.  Unknown flag bits: ATTN_ERR_SHAPE.
+ */
+enum { ATTN_CAUSAL = 1 };
+int attn_fwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int flags,
+                const void* q, const void* k, const void* v, const uint8_t* key_mask, void* out,
+                float* lse, void* stream);
+int attn_bwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int flags,
+                const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                const float* lse, const float* delta, const void* dout, void* dq, void* dk,
+                void* dv, void* stream);
+
+/*
  * Packed variable-length forward (the FA3-varlen path of diffusers PR #14834,
  * "Model test coverage"): nseq sequences packed back to back in q, k, v
  * (T, H, D); sequence n owns rows [cu[n], cu[n+1]) and attends only to its own
@@ -167,6 +184,15 @@ int attn_bwd_accum(int B, int Sq, int Sk, int H, int D, float scale, const void*
 
 /* dst[i] = bf16(src[i]), round to nearest even, for n fp32 values (device pointers). */
 int attn_cast_bf16(int64_t n, const float* src, void* dst, void* stream);
+
+/* Varlen with flags (ATTN_CAUSAL applies inside each sequence). */
+int attn_varlen_fwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                       int H, int D, float scale, int flags, const void* q, const void* k,
+                       const void* v, void* out, float* lse, void* stream);
+int attn_varlen_bwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                       int H, int D, float scale, int flags, const void* q, const void* k,
+                       const void* v, const float* lse, const float* delta, const void* dout,
+                       void* dq, void* dk, void* dv, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,10 +35,11 @@ def test_exports_every_declared_symbol(L):
     names = declared()
     assert {"attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_varlen_fwd",
             "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum", "attn_cast_bf16",
-            "attn_fwd_gqa", "attn_bwd_gqa"} <= set(names)
+            "attn_fwd_gqa", "attn_bwd_gqa", "attn_fwd_ex", "attn_bwd_ex", "attn_varlen_fwd_ex",
+            "attn_varlen_bwd_ex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 3
+    assert L.attn_abi_version() == 4
     assert L.attn_status_str(0) == b"ok"
     assert L.attn_status_str(4) == b"invalid cu_seqlens"
 
@@ -149,6 +150,14 @@ def test_gqa_validation(L):
         assert f(H=0, Hk=0) == OK
         assert f(B=0) == OK
     assert L.attn_fwd_gqa(1, 8, 8, 8, 2, 64, 0.125, P, None, P, None, P, P, None) == NULL
+    # flags: only ATTN_CAUSAL (1) is defined
+    assert L.attn_fwd_ex(1, 8, 8, 8, 2, 64, 0.125, 2, P, P, P, None, P, P, None) == SHAPE
+    assert L.attn_bwd_ex(1, 8, 8, 8, 2, 64, 0.125, 4, P, P, P, None, P, P, P, P, P, P, None) == SHAPE
+    assert L.attn_fwd_ex(0, 8, 8, 8, 2, 64, 0.125, 1, P, P, P, None, P, P, None) == OK
+    arr = np.array([0, 4], dtype=np.int32)
+    cu = arr.ctypes.data_as(ctypes.c_void_p)
+    assert L.attn_varlen_fwd_ex(1, cu, P, 2, 64, 0.1, 8, P, P, P, P, P, None) == SHAPE
+    assert L.attn_varlen_bwd_ex(1, cu, P, 2, 64, 0.1, 8, P, P, P, P, P, P, P, P, P, None) == SHAPE
 
 
 def _cu(vals):
