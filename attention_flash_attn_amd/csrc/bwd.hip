@@ -16,7 +16,7 @@
 //
 // dK/dV workgroup: 8 waves, 128 keys.  The keys' K and V rows sit in LDS for the whole
 // loop; query tiles of 64 rows (Q, dO, LSE, delta) are double-buffered in LDS, filled
-// asynchronously by global_load_lds into XOR-swizzled rows (tile.hpp).  Wave w owns key
+// asynchronously by buffer loads into XOR-swizzled LDS rows (tile.hpp).  Wave w owns key
 // block w%4 (32 keys, one per lane of the score tile S = Q K^T) and query sub-tile w/4 of
 // every tile, with its dK^T, dV^T accumulators in registers across the loop; the two
 // waves of a key block add their partial sums through LDS at the end.  Q^T and dO^T

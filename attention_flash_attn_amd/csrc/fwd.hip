@@ -11,8 +11,8 @@
 //    row statistics (max, sum, LSE) are per-lane values; the only cross-lane
 //    step is one exchange between the two 32-lane halves.
 //  * K/V tiles of 64 keys are double-buffered in LDS and filled asynchronously
-//    by global_load_lds (tile j+1 is in flight while tile j is consumed; one
-//    barrier per tile).  Tiles are unpadded and XOR-swizzled (tile.hpp) so the
+//    by buffer loads into LDS (tile j+1 is in flight while tile j is consumed; one
+//    barrier per tile), one copy instruction after each of the first score MFMAs.  Tiles are unpadded and XOR-swizzled (tile.hpp) so the
 //    row reads of K and the transposing reads of V are bank-conflict free.
 //    K rows are stored permuted (kRowPerm) so that the exponentiated score
 //    registers are directly the B operand of O^T += V^T P^T.
@@ -24,6 +24,8 @@
 //  * Tiles whose keys are all masked are skipped; in partially valid tiles (a
 //    ragged tail or a mask edge) a branch taken only there sets the excluded
 //    scores to -inf, so full tiles carry no per-element mask work.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -120,14 +122,38 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // Tiles that need per-element masking: not every key valid (mask, ragged tail), or, when
   // causal, some key of the tile after some query row of the workgroup.
   auto needs_mask = [&](int k0, uint64_t vw) { return vw != ~0ull || (p.causal && k0 + BN - 1 > qb); };
-  auto compute = [&](const char* kt, const char* vt, int k0, uint64_t vw) {
-    f32x16 sacc[2];
+  // The copy of the next tile (n0 >= 0: its first key; a tile whose keys all exist) is
+  // issued one instruction at a time between the score MFMAs: each copy instruction holds
+  // the wave at issue for a while, and there the matrix unit still works on the MFMA
+  // before it.
+  auto compute = [&](auto spread, const char* kt, const char* vt, int k0, uint64_t vw, int n0,
+                     char* kn, char* vn) {
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    constexpr int NI = decltype(kld)::NI;
+    const auto krs = kld.rsrc(kbase, rsk, n0), vrs = vld.rsrc(vbase, rsk, n0);
+    static_assert(2 * NI <= 2 * NKS, "one copy instruction per score MFMA at most");
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
+        const int n = 2 * ks + kb;
+        if (decltype(spread)::value && n < 2 * NI) {
+          if (n < NI)
+            kld.issue_one_full(n, kn, krs);
+          else
+            vld.issue_one_full(n - NI, vn, vrs);
+        }
+      }
+    if (decltype(spread)::value) {
+      // K row reads two MFMAs ahead, one copy instruction after each of the first MFMAs.
+      ATTN_SCHED(kSchedDSRead, 2);
+#pragma unroll
+      for (int n = 0; n < 2 * NKS; ++n) {
+        ATTN_SCHED(kSchedMFMA, 1);
+        if (n < 2 * NI) ATTN_SCHED(kSchedVMEMRead, 1);
+        if (n + 2 < 2 * NKS) ATTN_SCHED(kSchedDSRead, 1);
+      }
     }
     if (needs_mask(k0, vw)) {
       keep_branch();
@@ -203,9 +229,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     if (more) {
       vw_next = kv.word((j + 1) * BN, mbytes);
       mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
-      issue((j + 1) * BN, kn, vn);
     }
-    if (vw != 0) compute(kt, vt, j * BN, vw);
+    // The next tile's copy: spread over the score MFMAs when there are any and the tile is
+    // whole, else all at once here.
+    const bool spread = more && vw != 0 && (j + 2) * BN <= nk;
+    if (more && !spread) issue((j + 1) * BN, kn, vn);
+    if (spread)
+      compute(std::true_type{}, kt, vt, j * BN, vw, (j + 1) * BN, kn, vn);
+    else if (vw != 0)
+      compute(std::false_type{}, kt, vt, j * BN, vw, 0, kn, vn);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;

@@ -1,5 +1,5 @@
 // tile.hpp -- LDS tiles for gfx950: unpadded rows, 16-byte chunks XOR-swizzled, filled
-// asynchronously by global_load_lds_dwordx4.
+// asynchronously by buffer_load_dwordx4 ... lds.
 //
 // A tile holds R rows of D bf16 (2*D bytes per row, no padding).  The 16-byte
 // chunk c of row r is stored at chunk position c ^ swz(r).  The swizzle makes the
@@ -11,7 +11,7 @@
 //    16-byte bank groups.
 // swz depends only on r & 15, so moving by a multiple of 16 rows keeps offsets.
 //
-// global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at M0 + 16*l, i.e. one
+// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at M0 + 16*l, i.e. one
 // instruction fills 1 KiB of LDS contiguously; the swizzle is applied on the
 // global side by choosing which chunk each lane fetches.
 #pragma once
@@ -20,6 +20,9 @@
 namespace attn {
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Word 3 of a raw buffer resource (stride 0, byte-addressed, 32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 __device__ __forceinline__ int swz(int r) {
@@ -51,12 +54,14 @@ __device__ __forceinline__ bf16x8 lds_tr8(const char* tile, int off_lo, int off_
                 lds_read_tr16(reinterpret_cast<const bf16*>(tile + off_hi)));
 }
 
-// Asynchronous tile copy with NW waves.  Lane-dependent parts of the global
-// addresses are fixed per kernel, so they are computed once: off[i] is the byte
-// offset, from the global address of the tile's first row, of the 16-byte chunk
-// this lane fetches with its i-th instruction.  row_of(r) maps tile row r to its
-// row offset within the tile (a permutation of 0..ROWS-1).  A tile that runs past
-// the last valid row re-reads that row instead (a tail tile only).
+// Asynchronous tile copy with NW waves, by buffer_load_dwordx4 ... lds: the tile's first
+// row is the base of a buffer resource built per tile in scalar registers, so each lane
+// keeps only 32-bit offsets.  Lane-dependent parts of the offsets are fixed per kernel,
+// so they are computed once: off[i] is the byte offset, from the tile's first row, of the
+// 16-byte chunk this lane fetches with its i-th instruction.  row_of(r) maps tile row r
+// to its row offset within the tile (a permutation of 0..ROWS-1).  A tile that runs past
+// the last valid row re-reads that row instead (a tail tile only), so every access stays
+// inside the tensor.
 template <int D, int ROWS, int NW>
 struct TileLoader {
   static constexpr int CPR = D / 8;            // chunks per row
@@ -76,25 +81,41 @@ struct TileLoader {
     }
   }
 
+  // Buffer resource whose byte 0 is row row0 of the tensor whose row 0 (this head) is at
+  // `base`, covering the ROWS rows of a tile (the callers keep ROWS * 2 * rs < 2^32).
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16* base, long rs, int row0) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (long)row0 * rs), (short)0,
+                                             (int)(ROWS * 2 * rs), kBufferFlags);
+  }
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char* tile, int i, uint32_t o) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (wave + i * NW) * 1024), 16, o, 0, 0, 0);
+  }
+
+  // Instruction i (0 <= i < NI) of issue() alone, for a tile whose rows all exist
+  // (row0 + ROWS <= nrows), so that a kernel can spread the copy between its matrix
+  // instructions.
+  __device__ __forceinline__ void issue_one_full(int i, char* tile, __amdgpu_buffer_rsrc_t r) const {
+    load(r, tile, i, off[i]);
+  }
+
   // Copy rows [row0, row0 + ROWS) of the tensor whose row 0 (this head) is at `base`;
   // only rows < nrows exist.
   template <typename RowOf>
   __device__ __forceinline__ void issue(char* tile, const bf16* base, long rs, int row0, int nrows,
                                         RowOf row_of) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const char* g = reinterpret_cast<const char*>(base + (long)row0 * rs);
+    const __amdgpu_buffer_rsrc_t r = rsrc(base, rs, row0);
     if (row0 + ROWS <= nrows) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        __builtin_amdgcn_global_load_lds(g + off[i], (lds_void*)(tile + (wave + i * NW) * 1024), 16, 0, 0);
+      for (int i = 0; i < NI; ++i) load(r, tile, i, off[i]);
     } else {
-      const int lane = threadIdx.x & 63, last = nrows - 1 - row0;
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, last = nrows - 1 - row0;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int r = (wave + i * NW) * RPI + lane / CPR;
-        const int want = row_of(r), have = min(want, last);
-        const long o = (long)off[i] + 2 * (long)(have - want) * rs;
-        __builtin_amdgcn_global_load_lds(g + o, (lds_void*)(tile + (wave + i * NW) * 1024), 16, 0, 0);
+        const int rr = (wave + i * NW) * RPI + lane / CPR;
+        const int want = row_of(rr), have = min(want, last);
+        load(r, tile, i, (uint32_t)((long)off[i] + 2 * (long)(have - want) * rs));
       }
     }
   }
