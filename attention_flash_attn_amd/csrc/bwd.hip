@@ -173,9 +173,10 @@ __device__ __forceinline__ void perm_tr_offsets(int lane, int (&off)[D / 32][2])
 
 // dK/dV: 8 waves, 128 keys.  Wave w owns key block w%4 (32 keys, one per lane) and
 // query sub-tile w/4 of every 64-row tile, so two waves accumulate partial dK/dV for
-// the same keys; they are summed through LDS at the end.  K and V stay in LDS (not in
-// registers), which keeps a wave within 256 registers: two waves per SIMD, so one
-// wave's MFMAs run while the other does its softmax VALU work.
+// the same keys; they are summed through LDS at the end.  The wave's K fragments (the B
+// operand of S = Q K^T, 32 registers) are read from LDS once and kept in registers for the
+// whole loop; V stays in LDS, which keeps a wave within 256 registers: two waves per SIMD,
+// so one wave's MFMAs run while the other does its softmax VALU work.
 template <int D, bool VARLEN, bool ACC>
 __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, DkdvSmem<D>& sm) {
   constexpr int BN = DkdvSmem<D>::BN, BQ = DkdvSmem<D>::BQ, NW = 8;
@@ -260,6 +261,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
   const float c2 = p.c2;
   const int qr = sub * 32 * RB, kr = kblk * 32 * RB;
+  bf16x8 kreg[NKS];  // this wave's 32 keys as the B operand of S = Q K^T, one per ks
 
   // One 32x32 (query x key) step: scores S = Q K^T and dP = dO V^T (one key per lane),
   // weights P = exp(scale S - LSE) and dS = P (dP - delta), then dV^T += dO^T P and
@@ -274,7 +276,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     f32x16 s = row_values16(lt + 32 * sub + 8 * hl), dp = row_values16(dt + 32 * sub + 8 * hl);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      s = mfma32(lds_row16(qt, qr + qoff[ks]), lds_row16(kt, kr + qoff[ks]), s);
+      s = mfma32(lds_row16(qt, qr + qoff[ks]), kreg[ks], s);
     if (p.causal && q0 < kb0 + BN - 1) {
       keep_branch();
       // A tile on the diagonal: P = 0 where this lane's key comes after register r's row.
@@ -322,6 +324,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   }
   wait_tile_loads();
   __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) kreg[ks] = lds_row16(sm.k, kr + qoff[ks]);
   for (int j = 0; j < ntiles; j += 2) {
     step(j, sm.k, sm.v, sm.q[0], sm.o[0], sm.l[0], sm.d[0], sm.q[1], sm.o[1], sm.l[1], sm.d[1]);
     if (j + 1 < ntiles)

@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, Wan shard N=27280 H=10 D=128"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+# executed / algorithmic MFMA FLOPs of one fwd+bwd step: (2 + 7) / (2 + 5) products
+EXECUTED_PER_ALGORITHMIC = 9.0 / 7.0
 PEAK_HBM_GBS = 8000.0
 
 
@@ -341,6 +343,10 @@ def main():
         "config": {"workload": describe(w), "batch": B, "seq_len": S, "heads": H,
                    "head_dim": D, "parallelism": "none"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        # MFMA work as executed: the forward's 2 products and the backward's 7 (dK/dV: 4,
+        # dQ: 3, of which 2 recompute S and dP), against the 5 the algorithmic count credits
+        "executed_tflops": round(EXECUTED_PER_ALGORITHMIC * value, 2),
+        "pct_bf16_peak_executed": round(100 * EXECUTED_PER_ALGORITHMIC * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"attn_fwd": round(fwd_ms, 4), "attn_bwd_preprocess": round(pre_ms, 4),
                        "attn_bwd": round(bwd_ms, 4)},
         "fwd_tflops": round(f_fwd / (fwd_ms / 1e3) / 1e12, 2),

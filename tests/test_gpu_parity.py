@@ -113,6 +113,28 @@ def test_page_shapes(A, name):
         assert e <= 2 * a, (errs, anchor)
 
 
+def test_hs_layout_probe_fails_parity(A):
+    """Negative check of the bar itself (diffusers PR #14341, "Test"): with H == S the
+    double-transposed K/V still have the right shape, so only values can reveal it.  The
+    GPU backward fed K and V with S and H swapped (forward, out and LSE from the correct
+    inputs) must miss the oracle's gradients by far more than the tolerance, by as much as
+    the page's buggy path did."""
+    import torch
+    w = I.WORKLOADS["probe_hs16"]
+    t = I.draw_workload(w)
+    g, r = gpu_dense(A, t), oracle_dense(t)
+    q, k, v, do = (to_dev(x) for x in (t.q, t.k, t.v, t.do))
+    kt, vt = (x.transpose(1, 2).contiguous() for x in (k, v))
+    dq, dk, dv = A.attn_bwd(q, kt, vt, g["lse"], g["delta"], do)
+    torch.cuda.synchronize()
+    page = json.load(open(os.path.join(GOLDEN, "page_reported_errors.json")))["probe_hs16"]
+    for n, x, bug in zip(("dq", "dk", "dv"), (dq, dk, dv),
+                         page["double_transposed_kv_max_abs_error_dq_dk_dv"]):
+        err = max_err(to_f64(x), r[n])
+        assert err > 50 * 2e-2 and err > 0.25 * np.max(np.abs(r[n])), (n, err)
+        assert bug / 5 < err < bug * 5, (n, err, bug)
+
+
 def test_scale_argument(A):
     t = I.small_case(1, 130, 130, 2, 64, seed=5)
     check_all(gpu_dense(A, t, scale=0.3), oracle_dense(t, scale=0.3), t)
