@@ -89,7 +89,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // Ask the scheduler for a group of n instructions of class `mask` next in the
 // current basic block (groups are filled in the order they are requested).
 #define ATTN_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)

@@ -5,17 +5,19 @@
 // PR, follow-up 1).  Keys excluded by the head-broadcast bool mask act as a
 // -inf bias (same PR, follow-up 2; diffusers PR #14834, "Unsupported cases").
 //
-// Design (one workgroup = 4 waves = 128 query rows of one (batch|sequence, head)):
+// Design (one workgroup = 8 waves = 256 query rows of one (batch|sequence, head), one
+// workgroup per CU):
 //  * Each wave keeps its 32 query rows in registers as the B operand of
 //    S^T = K Q^T, so the score tile arrives with one query per lane and all
 //    row statistics (max, sum, LSE) are per-lane values; the only cross-lane
 //    step is one exchange between the two 32-lane halves.
 //  * K/V tiles of 64 keys are double-buffered in LDS and filled asynchronously
-//    by buffer loads into LDS (tile j+1 is in flight while tile j is consumed; one
-//    barrier per tile), one copy instruction after each of the first score MFMAs.  Tiles are unpadded and XOR-swizzled (tile.hpp) so the
-//    row reads of K and the transposing reads of V are bank-conflict free.
+//    by buffer loads into LDS.  Tiles are unpadded and XOR-swizzled (tile.hpp) so
+//    the row reads of K and the transposing reads of V are bank-conflict free.
 //    K rows are stored permuted (kRowPerm) so that the exponentiated score
 //    registers are directly the B operand of O^T += V^T P^T.
+//  * Ping-pong: the two 4-wave groups (one wave of each per SIMD) run half a tile
+//    apart, so one group's MFMAs overlap the other group's softmax (see fwd_kernel).
 //  * Online softmax in base 2 with scale*log2(e) folded into one FMA.  The
 //    running max is only moved (and O, l rescaled) when the new tile max
 //    exceeds it by more than 8 (log2 units), so the rescale is rare; the
@@ -24,35 +26,41 @@
 //  * Tiles whose keys are all masked are skipped; in partially valid tiles (a
 //    ragged tail or a mask edge) a branch taken only there sets the excluded
 //    scores to -inf, so full tiles carry no per-element mask work.
-#include <type_traits>
-
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
 
 namespace attn {
 
+// Waves 0..3 (group A) and 4..7 (group B) sit one per SIMD each (wave w and w + 4 share a
+// SIMD), so every SIMD holds one wave of each group.
+// The loop runs in phases separated by workgroup barriers, and the two groups are half a
+// key tile apart: in each phase one group issues its MFMAs (O += P V for the previous
+// tile, then S^T = K Q^T for the current one) while the other does the softmax VALU work,
+// so the matrix units of a SIMD are fed by one wave while the other computes exponentials.
+//   phase 2j  : A: PV(j-1), S(j)      B: softmax(j-1); B issues the copies of K(j+1), V(j)
+//   phase 2j+1: A: softmax(j)         B: PV(j-1), S(j); B waits for its copies
+// K(j) is read in phases 2j, 2j+1 and V(j) in phases 2j+2, 2j+3, so two buffers each
+// suffice: a copy issued in phase 2j overwrites a tile last read in phase 2j-1.
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int RB = 2 * D;       // tile row bytes
-  constexpr int NKS = D / 16;     // MFMA reduction steps over the head dim
-  constexpr int NMB = D / 32;     // 32-row blocks of O^T
+__global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
+  constexpr int BM = kFwdBlockM, BN = 64;
+  constexpr int RB = 2 * D;
+  constexpr int NKS = D / 16;
+  constexpr int NMB = D / 32;
   __shared__ __attribute__((aligned(1024))) char sK0[BN * RB];
   __shared__ __attribute__((aligned(1024))) char sK1[BN * RB];
   __shared__ __attribute__((aligned(1024))) char sV0[BN * RB];
   __shared__ __attribute__((aligned(1024))) char sV1[BN * RB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_b = wave >= 4;
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int logical = xcd_remap(blockIdx.x, p.n_blocks);
-  // Causal: the last query tiles see the most keys, so they are dealt out first.
   const int qt = p.causal ? p.n_qtiles - 1 - logical % p.n_qtiles : logical % p.n_qtiles;
   const int rest = logical / p.n_qtiles;
-  // (outer, head) groups go head-major: each XCD's contiguous range of groups then holds
-  // every batch|sequence of a few heads, so the ranges carry equal work even when the
-  // sequences differ in length (varlen) or in valid keys (mask).
   const int head = rest / p.B, outer = rest % p.B;
   int qrow0, krow0, nq, nk;
   long lse_base;
@@ -71,25 +79,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     if (p.mask) mask = p.mask + (long)outer * p.Sk;
   }
   const int qb = qt * BM;
-  if (qb >= nq) return;  // block-uniform: a varlen tile past its sequence
+  if (qb >= nq) return;  // block-uniform
 
-  // Q/out rows hold H heads, K/V rows Hk; query head h reads key/value head h / G.
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int kvh = head / p.G;
   const bf16* kbase = p.k + (long)krow0 * rsk + (long)kvh * D;
   const bf16* vbase = p.v + (long)krow0 * rsk + (long)kvh * D;
 
-  // Query rows of this wave, as B operand slices over the head dim.
-  const int qrow = qb + wave * 32 + l32;
+  const int qw = qb + wave * 32;  // this wave's first query row
+  const int qrow = qw + l32;
   bf16x8 qreg[NKS];
   {
     const bf16* qp = p.q + ((long)qrow0 + min(qrow, nq - 1)) * rs + (long)head * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qreg[ks] = as_bf16x8(ld16(qp + 16 * ks));
   }
-
-  // Per-lane swizzled LDS offsets: K rows (MFMA A operand, one row per lane) and the
-  // transposing V reads (lane group g, source lane src; see lds_read_tr16).
   int koff[NKS], voff[NMB][2];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hl);
@@ -103,65 +107,75 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                                         32 * mb + 16 * (g & 1) + 4 * (src & 3));
   }
 
-  TileLoader<D, BN, 4> kld, vld;
+  TileLoader<D, BN, 4> kld, vld;  // used by group B only (waves 4..7)
   auto krow = [](int r) { return perm32_row(r); };
   auto vrow = [](int r) { return r; };
-  kld.init(rsk, krow);
-  vld.init(rsk, vrow);
-  auto issue = [&](int k0, char* kt, char* vt) {
-    kld.issue(kt, kbase, rsk, k0, nk, krow);
-    vld.issue(vt, vbase, rsk, k0, nk, vrow);
-  };
+  kld.init(rsk, krow, 4);
+  vld.init(rsk, vrow, 4);
 
   f32x16 oacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
+  f32x16 sacc[2];
+  bf16x8 pk[2][2];
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = p.c2;
 
-  // Tiles that need per-element masking: not every key valid (mask, ragged tail), or, when
-  // causal, some key of the tile after some query row of the workgroup.
-  auto needs_mask = [&](int k0, uint64_t vw) { return vw != ~0ull || (p.causal && k0 + BN - 1 > qb); };
-  // The copy of the next tile (n0 >= 0: its first key; a tile whose keys all exist) is
-  // issued one instruction at a time between the score MFMAs: each copy instruction holds
-  // the wave at issue for a while, and there the matrix unit still works on the MFMA
-  // before it.
-  auto compute = [&](auto spread, const char* kt, const char* vt, int k0, uint64_t vw, int n0,
-                     char* kn, char* vn) {
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    constexpr int NI = decltype(kld)::NI;
-    const auto krs = kld.rsrc(kbase, rsk, n0), vrs = vld.rsrc(vbase, rsk, n0);
-    static_assert(2 * NI <= 2 * NKS, "one copy instruction per score MFMA at most");
+  const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
+  const int ntiles = (kend + BN - 1) / BN;
+  const KeyValidity kv{mask, nk};
+  // Per wave: the key-validity word of the tile whose scores were formed last (0: nothing
+  // in it for this wave; its softmax and P V are skipped).
+  uint64_t vw_s = 0;
+  uint32_t mbytes = 0;
+  auto tile_word = [&](int j, uint32_t bytes) -> uint64_t __attribute__((always_inline)) {
+    // causal: a tile whose first key comes after this wave's last row is skipped
+    if (j >= ntiles || (p.causal && j * BN > qw + 31)) return 0;
+    return kv.word(j * BN, bytes);
+  };
+
+  // Operand reads run several MFMAs ahead (explicit schedule): with one wave per SIMD in
+  // its MFMA phase, nothing else hides an LDS read's latency from the matrix unit.
+  auto gemm_s = [&](const char* kt) __attribute__((always_inline)) {
+    sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
-        const int n = 2 * ks + kb;
-        if (decltype(spread)::value && n < 2 * NI) {
-          if (n < NI)
-            kld.issue_one_full(n, kn, krs);
-          else
-            vld.issue_one_full(n - NI, vn, vrs);
-        }
-      }
-    if (decltype(spread)::value) {
-      // K row reads two MFMAs ahead, one copy instruction after each of the first MFMAs.
-      ATTN_SCHED(kSchedDSRead, 2);
+    constexpr int AHEAD = 6, N = 2 * NKS;
+    ATTN_SCHED(kSchedDSRead, AHEAD);
 #pragma unroll
-      for (int n = 0; n < 2 * NKS; ++n) {
-        ATTN_SCHED(kSchedMFMA, 1);
-        if (n < 2 * NI) ATTN_SCHED(kSchedVMEMRead, 1);
-        if (n + 2 < 2 * NKS) ATTN_SCHED(kSchedDSRead, 1);
-      }
+    for (int n = 0; n < N; ++n) {
+      ATTN_SCHED(kSchedMFMA, 1);
+      if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 1);
     }
-    if (needs_mask(k0, vw)) {
+  };
+  auto gemm_pv = [&](const char* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const char* vb = vt + (32 * kb + 16 * t) * RB;
+          oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
+        }
+    constexpr int AHEAD = 4, N = 4 * NMB;  // MFMAs; two transposing reads each
+    ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      ATTN_SCHED(kSchedMFMA, 1);
+      if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 2);
+    }
+  };
+  auto softmax = [&](int k0, uint64_t vw) __attribute__((always_inline)) {
+    if (vw != ~0ull || (p.causal && k0 + BN - 1 > qw)) {
       keep_branch();
-      // Register r of half kb holds key k0 + 32kb + 16(r/8) + 8hl + r%8 (its bit in vw is
-      // that minus k0) of this lane's query row qrow.
+      // Register r of half kb holds key k0 + 32kb + 16(r/8) + 8hl + r%8 of row qrow.
       const uint64_t vl = vw >> (8 * hl);
       const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
-      const int last = p.causal ? qrow - k0 - 8 * hl : BN;  // largest visible key - k0 - 8hl
+      const int last = p.causal ? qrow - k0 - 8 * hl : BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -190,7 +204,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       m_run = mnew;
     }
     const float muse = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 pk[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -202,56 +215,56 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       pk[kb][0] = pack8(sacc[kb], 0);
       pk[kb][1] = pack8(sacc[kb], 8);
     }
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const char* vb = vt + (32 * kb + 16 * t) * RB;
-          oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
-        }
+  };
+  // MFMA phase of tile j: O += P(j-1) V(j-1), then S(j).  Group B then waits for the
+  // copies it issued in its previous phase.
+  auto gemm_phase = [&](int j, const char* __restrict__ kt, const char* __restrict__ vp)
+      __attribute__((always_inline)) {
+    if (vw_s != 0) gemm_pv(vp);  // vw_s: still the word of tile j-1
+    vw_s = tile_word(j, mbytes);
+    mbytes = kv.load((j + 1) * BN);  // clamped: unused past the last tile
+    if (vw_s != 0) gemm_s(kt);
+    if (grp_b) wait_tile_loads();
+  };
+  // VALU phase of tile j.  Group B first issues the copies of K(j+2) (into the buffer of
+  // K(j), whose last reader was its own MFMA phase) and V(j+1) (into the buffer of V(j-1)).
+  auto softmax_phase = [&](int j, char* __restrict__ kn, char* __restrict__ vn)
+      __attribute__((always_inline)) {
+    if (grp_b) {
+      if (j + 2 < ntiles) kld.issue(kn, kbase, rsk, (j + 2) * BN, nk, krow);
+      if (j + 1 < ntiles) vld.issue(vn, vbase, rsk, (j + 1) * BN, nk, vrow);
+    }
+    if (vw_s != 0) softmax(j * BN, vw_s);
+  };
+  // Both groups run the same sequence, group B one phase later (it passes one barrier
+  // before its first phase, group A one after its last), so register lifetimes at every
+  // barrier are the same for both.
+  // kc: the buffer of K(j) (and of K(j+2)), vp: the buffer of V(j-1) (and of V(j+1)).
+  auto pair = [&](int j, char* __restrict__ kc, char* __restrict__ vp) __attribute__((always_inline)) {
+    gemm_phase(j, kc, vp);
+    __syncthreads();
+    softmax_phase(j, kc, vp);
+    __syncthreads();
   };
 
-  // Causal: keys past the workgroup's last query row are never seen.
-  const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
-  const int ntiles = (kend + BN - 1) / BN;
-  uint64_t vw = 0;
-  const KeyValidity kv{mask, nk};
-  uint32_t mbytes = 0;  // raw mask bytes of tile j + 1 during step j
-  // Current and next tile buffers as distinct __restrict__ parameters: once inlined,
-  // the compiler can tell reads of one from the asynchronous copy into the other
-  // (without that it waits for the copy before the first LDS read).
-  auto step = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt,
-                  char* __restrict__ kn, char* __restrict__ vn) {
-    const bool more = j + 1 < ntiles;
-    uint64_t vw_next = 0;
-    if (more) {
-      vw_next = kv.word((j + 1) * BN, mbytes);
-      mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
-    }
-    // The next tile's copy: spread over the score MFMAs when there are any and the tile is
-    // whole, else all at once here.
-    const bool spread = more && vw != 0 && (j + 2) * BN <= nk;
-    if (more && !spread) issue((j + 1) * BN, kn, vn);
-    if (spread)
-      compute(std::true_type{}, kt, vt, j * BN, vw, (j + 1) * BN, kn, vn);
-    else if (vw != 0)
-      compute(std::false_type{}, kt, vt, j * BN, vw, 0, kn, vn);
-    wait_tile_loads();
-    __syncthreads();
-    vw = vw_next;
-  };
+  mbytes = kv.load(0);
   if (ntiles > 0) {
-    vw = kv.word(0, kv.load(0));
-    mbytes = kv.load(BN);
-    issue(0, sK0, sV0);
-    wait_tile_loads();
-  }
-  __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, sK0, sV0, sK1, sV1);
-    if (j + 1 < ntiles) step(j + 1, sK1, sV1, sK0, sV0);
+    if (grp_b) {
+      kld.issue(sK0, kbase, rsk, 0, nk, krow);
+      wait_tile_loads();
+    }
+    __syncthreads();
+    if (grp_b) {  // phase 0 (group A: MFMAs of tile 0)
+      if (1 < ntiles) kld.issue(sK1, kbase, rsk, BN, nk, krow);
+      vld.issue(sV0, vbase, rsk, 0, nk, vrow);
+      __syncthreads();
+    }
+    // even j: K(j) in sK0, V(j) in sV0; odd j: sK1, sV1
+    for (int j = 0; j <= ntiles; j += 2) {
+      pair(j, sK0, sV1);
+      if (j + 1 <= ntiles) pair(j + 1, sK1, sV0);
+    }
+    if (!grp_b) __syncthreads();
   }
 
   l_run = wave_sum_halves(l_run);
@@ -277,7 +290,7 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   if (p.n_blocks == 0) return hipSuccess;
   void* args[] = {const_cast<FwdParams*>(&p)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, VARLEN>), dim3(p.n_blocks),
-                         dim3(256), args, 0, stream);
+                         dim3(512), args, 0, stream);
 }
 
 hipError_t launch_fwd(int D, bool varlen, const FwdParams& p, hipStream_t stream) {

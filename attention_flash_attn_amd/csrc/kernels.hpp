@@ -50,7 +50,7 @@ struct BwdParams {
   float scale;
 };
 
-constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
+constexpr int kFwdBlockM = 256;   // query rows per forward workgroup (8 waves x 32)
 constexpr int kDqBlockM = 256;    // query rows per dQ workgroup
 constexpr int kDkvBlockN = 128;   // key rows per dK/dV workgroup
 

@@ -69,10 +69,13 @@ struct TileLoader {
   static constexpr int NI = ROWS * 2 * D / 1024 / NW;
   static_assert(ROWS * 2 * D % (1024 * NW) == 0, "tile must split evenly over the waves");
   uint32_t off[NI];
+  int wv;  // this wave's index among the NW copying waves (waves w0 .. w0 + NW - 1)
 
   template <typename RowOf>
-  __device__ __forceinline__ void init(long rs, RowOf row_of) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __device__ __forceinline__ void init(long rs, RowOf row_of, int w0 = 0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) - w0);
+    wv = wave;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = (wave + i * NW) * RPI + lane / CPR;
@@ -89,15 +92,7 @@ struct TileLoader {
   }
 
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char* tile, int i, uint32_t o) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (wave + i * NW) * 1024), 16, o, 0, 0, 0);
-  }
-
-  // Instruction i (0 <= i < NI) of issue() alone, for a tile whose rows all exist
-  // (row0 + ROWS <= nrows), so that a kernel can spread the copy between its matrix
-  // instructions.
-  __device__ __forceinline__ void issue_one_full(int i, char* tile, __amdgpu_buffer_rsrc_t r) const {
-    load(r, tile, i, off[i]);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (wv + i * NW) * 1024), 16, o, 0, 0, 0);
   }
 
   // Copy rows [row0, row0 + ROWS) of the tensor whose row 0 (this head) is at `base`;
@@ -110,10 +105,10 @@ struct TileLoader {
 #pragma unroll
       for (int i = 0; i < NI; ++i) load(r, tile, i, off[i]);
     } else {
-      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, last = nrows - 1 - row0;
+      const int lane = threadIdx.x & 63, last = nrows - 1 - row0;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int rr = (wave + i * NW) * RPI + lane / CPR;
+        const int rr = (wv + i * NW) * RPI + lane / CPR;
         const int want = row_of(rr), have = min(want, last);
         load(r, tile, i, (uint32_t)((long)off[i] + 2 * (long)(have - want) * rs));
       }
