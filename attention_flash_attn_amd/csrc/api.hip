@@ -168,8 +168,9 @@ static BwdParams bwd_params(int B, int Sq, int Sk, int H, int Hk, float scale, c
 }
 
 // Grid of the backward launch: per (outer, key/value head) the dQ workgroups of its G query
-// heads and its dK/dV workgroups, the longer kind first.  Work per workgroup: dK/dV 128 keys
-// x G * nq query rows x 4 products, dQ 256 query rows x nk keys x 3 products.
+// heads and its dK/dV workgroups; the kernel starts every workgroup of the longer kind
+// before the shorter ones.  Work per workgroup: dK/dV 128 keys x G * nq query rows x 4
+// products, dQ 256 query rows x nk keys x 3 products.
 static void bwd_grid(BwdParams& p, int nq, int nk, int outer) {
   p.n_kv_tiles = (int)cdiv(nk, attn::kDkvBlockN);
   p.n_q_tiles = (int)cdiv(nq, attn::kDqBlockM);

@@ -44,7 +44,7 @@ struct BwdParams {
   int causal;      // query row i sees keys j <= i only (within its sequence)
   int n_kv_tiles;  // dK/dV workgroups per (outer, key/value head)
   int n_q_tiles;   // dQ workgroups per (outer, query head)
-  int dkdv_first;  // grid order inside a group: the longer workgroup kind first
+  int dkdv_first;  // grid order: the dK/dV workgroups first (they are the longer kind)
   int n_blocks;
   float c2;     // scale * log2(e)
   float scale;
