@@ -600,7 +600,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   const bool kv = kv_first ? L < n_kv_all : L >= n_q_all;
   const int r = kv ? (kv_first ? L : L - n_q_all) : (kv_first ? L - n_kv_all : L);
   int group, idx;
-  if (kv) {
+  if (p.causal) {
+    // Causal workgroups differ in length by tile (dK/dV: the first key tiles, dQ: the last
+    // query tiles see the most): within each kind, the longest tile of every group first.
+    if (kv) {
+      group = r % ngroups;
+      idx = r / ngroups;
+    } else {
+      const int rank = r / (ngroups * p.G), rest = r % (ngroups * p.G);
+      group = rest / p.G;
+      idx = (rest % p.G) * p.n_q_tiles + rank;
+    }
+  } else if (kv) {
     group = r / p.n_kv_tiles;
     idx = r % p.n_kv_tiles;
   } else {

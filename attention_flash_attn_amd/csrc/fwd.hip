@@ -58,9 +58,20 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const bool grp_b = wave >= 4;
   const int hl = lane >> 5, l32 = lane & 31;
 
-  const int logical = xcd_remap(blockIdx.x, p.n_blocks);
-  const int qt = p.causal ? p.n_qtiles - 1 - logical % p.n_qtiles : logical % p.n_qtiles;
-  const int rest = logical / p.n_qtiles;
+  int qt, rest;
+  if (p.causal) {
+    // The last query tiles see the most keys: those of every (head, outer) first, over the
+    // whole grid in plain block order (dealt round-robin to the XCDs).
+    const int nbh = p.B * p.H;
+    qt = p.n_qtiles - 1 - (int)blockIdx.x / nbh;
+    rest = (int)blockIdx.x % nbh;
+  } else {
+    // Equal workgroups: consecutive query tiles of one head share an XCD range (and its
+    // L2 holds that head's K and V); plain block order measured 2.6% slower.
+    const int logical = xcd_remap(blockIdx.x, p.n_blocks);
+    qt = logical % p.n_qtiles;
+    rest = logical / p.n_qtiles;
+  }
   const int head = rest / p.B, outer = rest % p.B;
   int qrow0, krow0, nq, nk;
   long lse_base;
