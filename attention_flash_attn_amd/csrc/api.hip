@@ -82,6 +82,38 @@ const char* attn_status_str(int status) {
 
 int attn_abi_version(void) { return kAbiVersion; }
 
+// Compute units of the device that runs `stream` (cached per device).
+static int cu_count(hipStream_t stream) {
+  static int cached[64];
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) dev = 0;
+  if (dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Grid of the forward launch: one block per whole query tile, except that when the last
+// round of blocks would fill at most half of the CUs, those last `rem` tiles run as 2 rem
+// split blocks (half the rows, the keys shared out between the two wave groups), which
+// take about half as long.  Only where the tiles are of equal length (`may_split`: dense,
+// non-causal).
+static void fwd_grid(FwdParams& p, int tiles, bool may_split, hipStream_t stream) {
+  p.n_full = tiles;
+  p.n_blocks = tiles;
+  if (!may_split) return;
+  const int ncu = cu_count(stream);
+  const int rem = tiles % ncu;
+  if (tiles >= ncu && rem > 0 && 2 * rem <= ncu) {
+    p.n_full = tiles - rem;
+    p.n_blocks = p.n_full + 2 * rem;
+  }
+}
+
 int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, void* out, float* lse, void* stream) {
   return attn_fwd_ex(B, Sq, Sk, H, H, D, scale, 0, q, k, v, key_mask, out, lse, stream);
@@ -121,7 +153,7 @@ int attn_fwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int fl
   p.G = H / Hk;
   p.causal = flags & ATTN_CAUSAL;
   p.n_qtiles = (int)cdiv(Sq, attn::kFwdBlockM);
-  p.n_blocks = p.n_qtiles * H * B;
+  fwd_grid(p, p.n_qtiles * H * B, !p.causal, static_cast<hipStream_t>(stream));
   p.c2 = scale * attn::kLog2e;
   return status_of(attn::launch_fwd(D, false, p, static_cast<hipStream_t>(stream)));
 }
@@ -305,7 +337,7 @@ int attn_varlen_fwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
   p.G = 1;
   p.causal = flags & ATTN_CAUSAL;
   p.n_qtiles = (int)cdiv(maxlen, attn::kFwdBlockM);
-  p.n_blocks = p.n_qtiles * H * nseq;
+  fwd_grid(p, p.n_qtiles * H * nseq, false, static_cast<hipStream_t>(stream));
   p.c2 = scale * attn::kLog2e;
   return status_of(attn::launch_fwd(D, true, p, static_cast<hipStream_t>(stream)));
 }

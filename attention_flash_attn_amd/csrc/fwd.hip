@@ -48,18 +48,32 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   constexpr int RB = 2 * D;
   constexpr int NKS = D / 16;
   constexpr int NMB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char sK0[BN * RB];
-  __shared__ __attribute__((aligned(1024))) char sK1[BN * RB];
-  __shared__ __attribute__((aligned(1024))) char sV0[BN * RB];
-  __shared__ __attribute__((aligned(1024))) char sV1[BN * RB];
+  constexpr int TILE = BN * RB;  // bytes of one K or V tile
+  // Ping-pong workgroups use the first four tiles; a split workgroup (below) gives each
+  // wave group four of its own.
+  __shared__ __attribute__((aligned(1024))) char smem[8 * TILE];
+  char* const sK0 = smem;
+  char* const sK1 = smem + TILE;
+  char* const sV0 = smem + 2 * TILE;
+  char* const sV1 = smem + 3 * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool grp_b = wave >= 4;
   const int hl = lane >> 5, l32 = lane & 31;
 
-  int qt, rest;
-  if (p.causal) {
+  // Blocks from p.n_full on are split workgroups: the two halves (128 rows) of the query
+  // tiles n_full, n_full + 1, ..., each with its keys shared out between the two wave
+  // groups (see the split loop below).  They only exist for a non-causal dense launch whose
+  // last round of full workgroups would leave most CUs idle.
+  const bool split = (int)blockIdx.x >= p.n_full;
+  int qt, rest, half = 0;
+  if (split) {
+    const int b = (int)blockIdx.x - p.n_full, t = p.n_full + b / 2;
+    half = b & 1;
+    qt = t % p.n_qtiles;
+    rest = t / p.n_qtiles;
+  } else if (p.causal) {
     // The last query tiles see the most keys: those of every (head, outer) first, over the
     // whole grid in plain block order (dealt round-robin to the XCDs).
     const int nbh = p.B * p.H;
@@ -68,7 +82,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   } else {
     // Equal workgroups: consecutive query tiles of one head share an XCD range (and its
     // L2 holds that head's K and V); plain block order measured 2.6% slower.
-    const int logical = xcd_remap(blockIdx.x, p.n_blocks);
+    const int logical = xcd_remap(blockIdx.x, p.n_full);
     qt = logical % p.n_qtiles;
     rest = logical / p.n_qtiles;
   }
@@ -89,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     lse_base = ((long)outer * p.H + head) * p.Sq;
     if (p.mask) mask = p.mask + (long)outer * p.Sk;
   }
-  const int qb = qt * BM;
+  const int qb = qt * BM + half * (BM / 2);  // first row of this workgroup
   if (qb >= nq) return;  // block-uniform
 
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
@@ -97,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const bf16* kbase = p.k + (long)krow0 * rsk + (long)kvh * D;
   const bf16* vbase = p.v + (long)krow0 * rsk + (long)kvh * D;
 
-  const int qw = qb + wave * 32;  // this wave's first query row
+  const int qw = qb + (split ? wave & 3 : wave) * 32;  // this wave's first query row
   const int qrow = qw + l32;
   bf16x8 qreg[NKS];
   {
@@ -258,6 +272,73 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     __syncthreads();
   };
 
+  if (split) {
+    // Split workgroup: both groups take the same 128 rows (wave w and w + 4 the same 32),
+    // group g the key tiles [g hn, (g + 1) hn), each with its own double-buffered K/V tiles
+    // and its own copies; both groups step in lockstep (one barrier per step).  The two
+    // partial softmax states are then combined through LDS.
+    const int g = grp_b ? 1 : 0;
+    const int hn = (ntiles + 1) / 2, t0 = g * hn, t1 = min(ntiles, t0 + hn);
+    char* const gb = smem + 4 * TILE * g;
+    TileLoader<D, BN, 4> gk, gv;
+    gk.init(rsk, krow, 4 * g);
+    gv.init(rsk, vrow, 4 * g);
+    uint64_t vw = 0;
+    auto sstep = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt,
+                     char* __restrict__ kn, char* __restrict__ vn) __attribute__((always_inline)) {
+      const bool more = j + 1 < t1;
+      uint64_t vw_next = 0;
+      if (more) {
+        vw_next = tile_word(j + 1, mbytes);
+        mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
+        gk.issue(kn, kbase, rsk, (j + 1) * BN, nk, krow);
+        gv.issue(vn, vbase, rsk, (j + 1) * BN, nk, vrow);
+      }
+      if (j < t1 && vw != 0) {
+        gemm_s(kt);
+        softmax(j * BN, vw);
+        gemm_pv(vt);
+      }
+      wait_tile_loads();
+      __syncthreads();
+      vw = vw_next;
+    };
+    if (t0 < t1) {
+      vw = tile_word(t0, kv.load(t0 * BN));
+      mbytes = kv.load((t0 + 1) * BN);
+      gk.issue(gb, kbase, rsk, t0 * BN, nk, krow);
+      gv.issue(gb + 2 * TILE, vbase, rsk, t0 * BN, nk, vrow);
+    }
+    wait_tile_loads();
+    __syncthreads();
+    for (int s = 0; s < hn; s += 2) {
+      sstep(t0 + s, gb, gb + 2 * TILE, gb + TILE, gb + 3 * TILE);
+      if (s + 1 < hn) sstep(t0 + s + 1, gb + TILE, gb + 3 * TILE, gb, gb + 2 * TILE);
+    }
+    // Combine: group B parks (m, l, O) per lane, group A merges and stores.
+    l_run = wave_sum_halves(l_run);
+    float* red = reinterpret_cast<float*>(smem) + (wave & 3) * 64 * (16 * NMB + 2);
+    if (grp_b) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(mb * 16 + r) * 64 + lane] = oacc[mb][r];
+      red[16 * NMB * 64 + lane] = m_run;
+      red[(16 * NMB + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (grp_b) return;
+    const float mb_ = red[16 * NMB * 64 + lane], lb = red[(16 * NMB + 1) * 64 + lane];
+    const float m = fmaxf(m_run, mb_);
+    const float a = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float b = mb_ == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb_ - m);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[mb][r] = a * oacc[mb][r] + b * red[(mb * 16 + r) * 64 + lane];
+    l_run = a * l_run + b * lb;
+    m_run = m;
+  } else {
   mbytes = kv.load(0);
   if (ntiles > 0) {
     if (grp_b) {
@@ -277,8 +358,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     }
     if (!grp_b) __syncthreads();
   }
-
   l_run = wave_sum_halves(l_run);
+  }
+
   if (qrow < nq) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     bf16* op = p.out + ((long)qrow0 + qrow) * rs + (long)head * D + 4 * hl;

@@ -135,6 +135,46 @@ def test_hs_layout_probe_fails_parity(A):
         assert bug / 5 < err < bug * 5, (n, err, bug)
 
 
+def _cu_count():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("D,B,Hk,lens", [(128, 1, None, None), (64, 1, None, None),
+                                         (128, 2, None, (1500, 2048)), (128, 1, 11, None)],
+                         ids=["D128", "D64", "mask", "gqa"])
+def test_split_tail_workgroups(A, D, B, Hk, lens):
+    """Forward grids whose last round would fill at most half the CUs run those last query
+    tiles as split workgroups (128 rows each, keys shared out between the two wave groups,
+    partial softmax states combined in LDS).  S = 2048 (8 tiles of 256 rows) and
+    B * H = ncu / 8 + 1 (x2 batches) leave 8 (16) such tiles: the last (outer, head) groups
+    in block order.  Their rows, and those of a whole-tile head, against the oracle."""
+    import torch
+    ncu = _cu_count()
+    S = 2048
+    H = (ncu // 8 + 1) if B == 1 else (ncu // 16 + 1)
+    tiles = 8 * H * B
+    assert tiles >= ncu and 0 < tiles % ncu <= ncu // 2, (tiles, ncu)
+    t = I.small_case(B, S, S, H, D, seed=600 + D + B, valid_lens=lens, Hk=Hk)
+    g = gpu_dense(A, t)
+    g2 = gpu_dense(A, t)
+    for n in ("out", "lse"):
+        assert torch.equal(g[n], g2[n]), f"{n} not deterministic"
+    q, k, v = (f64(x) for x in (t.q, t.k, t.v))
+    G = 1 if Hk is None else H // Hk
+    n_split = tiles % ncu
+    # tile t covers (rest = t // 8, query tile t % 8); rest = head * B + b
+    split_rests = sorted({(tiles - n_split + i) // 8 for i in range(n_split)})
+    for rest in split_rests[-2:] + [0]:
+        h, b = rest // B, rest % B
+        kh = h // G
+        m = None if t.key_mask is None else t.key_mask[b:b + 1]
+        o_r, l_r = oracle.attn_fwd(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, kh:kh + 1],
+                                   v[b:b + 1, :, kh:kh + 1], m)
+        assert_parity(f"out[b{b},h{h}]", to_f64(g["out"][b:b + 1, :, h:h + 1]), o_r)
+        assert_lse(to_f64(g["lse"][b:b + 1, h:h + 1]), l_r)
+
+
 def test_scale_argument(A):
     t = I.small_case(1, 130, 130, 2, 64, seed=5)
     check_all(gpu_dense(A, t, scale=0.3), oracle_dense(t, scale=0.3), t)
@@ -264,11 +304,13 @@ def test_wan_shard_sampled(A):
     S = w.S
     rows = np.unique(np.concatenate([[0, 1, S - 16, S - 1], rng.integers(0, S, 28)]))
     cols = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 30)]))
-    for h in (0, 7):
+    # head 9, rows 15616.. : the forward's split workgroups (the last 46 of 1070 query tiles)
+    rows9 = np.unique(np.concatenate([[15616, 15743, 15744, 27279], rng.integers(15616, S, 12)]))
+    for h, rws in ((0, rows), (7, rows), (9, rows9)):
         q, k, v, do = (f64(x[:, :, h:h + 1]) for x in (t.q, t.k, t.v, t.do))
         gh = {n: to_f64(g[n][:, :, h:h + 1]) for n in ("out", "dq", "dk", "dv")}
         gh["lse"] = to_f64(g["lse"][:, h:h + 1])
-        _sampled_head_check(gh, q, k, v, do, rows, cols, f"[h{h}]")
+        _sampled_head_check(gh, q, k, v, do, rws, cols, f"[h{h}]")
     for h in range(w.H):
         do = f64(t.do[:, :, h:h + 1])
         gh = {n: to_f64(g[n][:, :, h:h + 1]) for n in ("dk", "dv")}
