@@ -26,6 +26,9 @@
 //  * Tiles whose keys are all masked are skipped; in partially valid tiles (a
 //    ragged tail or a mask edge) a branch taken only there sets the excluded
 //    scores to -inf, so full tiles carry no per-element mask work.
+//  * Split tail workgroups: when the grid's last round would fill at most half of
+//    the CUs, its query tiles run as pairs of 128-row workgroups whose wave groups
+//    share out the keys and combine their softmax states in LDS (see fwd_kernel).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -39,9 +42,11 @@ namespace attn {
 // tile, then S^T = K Q^T for the current one) while the other does the softmax VALU work,
 // so the matrix units of a SIMD are fed by one wave while the other computes exponentials.
 //   phase 2j  : A: PV(j-1), S(j)      B: softmax(j-1); B issues the copies of K(j+1), V(j)
-//   phase 2j+1: A: softmax(j)         B: PV(j-1), S(j); B waits for its copies
-// K(j) is read in phases 2j, 2j+1 and V(j) in phases 2j+2, 2j+3, so two buffers each
-// suffice: a copy issued in phase 2j overwrites a tile last read in phase 2j-1.
+//   phase 2j+1: A: softmax(j)         B: PV(j-1), S(j)
+// B's copies have landed when phase 2j ends (__syncthreads() waits for the wave's
+// outstanding loads before the barrier).  K(j) is read in phases 2j, 2j+1 and V(j) in
+// phases 2j+2, 2j+3, so two buffers each suffice: a copy issued in phase 2j overwrites a
+// tile last read in phase 2j-1.
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = 64;

@@ -61,14 +61,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wan_shard_hbm_traffic.json")
 
 
 def kernel_source_hash():
-    """Hash of the kernel sources; HBM counters recorded for another hash are stale."""
+    """Hash of the kernel sources with their // comments and blank lines removed (so that
+    comment edits keep recorded counters valid); HBM counters recorded for another hash
+    are stale."""
     import hashlib
+    import re
     h = hashlib.sha256()
     d = os.path.join(ROOT, "attention_flash_attn_amd", "csrc")
     for f in sorted(os.listdir(d)):
         h.update(f.encode())
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            code = [re.sub(r"\s*//.*$", "", line).rstrip() for line in fh]
+        h.update("\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 
