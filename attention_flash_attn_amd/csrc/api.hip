@@ -64,6 +64,25 @@ int check_varlen(int nseq, const int32_t* cu, int H, int D, float scale, int* T,
   return ATTN_OK;
 }
 
+// Sequences by length, longest first (stable), when there are few enough to list.
+attn::SeqOrder seq_order(int nseq, const int32_t* cu) {
+  attn::SeqOrder o{};
+  if (nseq <= 1 || nseq > attn::kMaxOrderedSeqs) return o;
+  o.n_order = nseq;
+  for (int n = 0; n < nseq; ++n) o.seq[n] = (int16_t)n;
+  for (int i = 1; i < nseq; ++i) {  // insertion sort, at most 64 entries
+    const int16_t x = o.seq[i];
+    const int len = cu[x + 1] - cu[x];
+    int j = i - 1;
+    while (j >= 0 && cu[o.seq[j] + 1] - cu[o.seq[j]] < len) {
+      o.seq[j + 1] = o.seq[j];
+      --j;
+    }
+    o.seq[j + 1] = x;
+  }
+  return o;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,6 +356,7 @@ int attn_varlen_fwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
   p.G = 1;
   p.causal = flags & ATTN_CAUSAL;
   p.n_qtiles = (int)cdiv(maxlen, attn::kFwdBlockM);
+  p.order = seq_order(nseq, cu_seqlens_host);
   fwd_grid(p, p.n_qtiles * H * nseq, false, static_cast<hipStream_t>(stream));
   p.c2 = scale * attn::kLog2e;
   return status_of(attn::launch_fwd(D, true, p, static_cast<hipStream_t>(stream)));
@@ -369,6 +389,7 @@ int attn_varlen_bwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
   BwdParams p = bwd_params(nseq, T, T, H, H, scale, q, k, v, nullptr, lse, delta, dout, dq, dk,
                            dv, cu_seqlens_dev);
   p.causal = flags & ATTN_CAUSAL;
+  p.order = seq_order(nseq, cu_seqlens_host);
   bwd_grid(p, maxlen, maxlen, nseq);
   return status_of(attn::launch_bwd(D, true, false, p, s));
 }

@@ -97,10 +97,11 @@ template <bool VARLEN>
 __device__ __forceinline__ Slice decode(const BwdParams& p, int group, int tile, int i) {
   Slice s;
   s.tile = tile;
-  // group = key/value head * B + outer (batch entry or sequence)
-  s.kvhead = group / p.B;
+  // group = key/value head * B + outer (batch entry), or for varlen sequence rank * Hk +
+  // key/value head, the longest sequence's groups first (see SeqOrder)
+  s.kvhead = VARLEN ? group % p.Hk : group / p.B;
   s.qhead = s.kvhead * p.G + i;
-  const int outer = group % p.B;
+  const int outer = VARLEN ? p.order(group / p.Hk) : group % p.B;
   s.mask = nullptr;
   if (VARLEN) {
     const int s0 = p.cu[outer], s1 = p.cu[outer + 1];

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     qt = logical % p.n_qtiles;
     rest = logical / p.n_qtiles;
   }
-  const int head = rest / p.B, outer = rest % p.B;
+  // varlen: sequence ranks, longest first (see SeqOrder)
+  const int head = rest / p.B, outer = VARLEN ? p.order(rest % p.B) : rest % p.B;
   int qrow0, krow0, nq, nk;
   long lse_base;
   const uint8_t* mask = nullptr;

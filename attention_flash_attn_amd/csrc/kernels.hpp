@@ -7,6 +7,16 @@ namespace attn {
 
 // Dense problems: outer index = batch, rows of batch b start at b*Sq (q) / b*Sk (k).
 // Varlen problems: outer index = sequence n, rows [cu[n], cu[n+1]); Sq = Sk = T.
+// Varlen launches order their sequences longest first (the workgroups of a sequence all
+// take about its length), for up to this many sequences; seq_order[r] is the sequence of
+// rank r.  With more sequences (n_order = 0) they run in their given order.
+constexpr int kMaxOrderedSeqs = 64;
+struct SeqOrder {
+  int n_order;  // 0: given order
+  int16_t seq[kMaxOrderedSeqs];
+  __device__ __forceinline__ int operator()(int r) const { return n_order ? seq[r] : r; }
+};
+
 struct FwdParams {
   const __bf16* q;
   const __bf16* k;
@@ -22,6 +32,7 @@ struct FwdParams {
   int n_full;    // blocks [0, n_full): whole query tiles; the rest: halves of tiles n_full...
   int n_blocks;
   float c2;  // scale * log2(e)
+  SeqOrder order;  // varlen only
 };
 
 struct BwdParams {
@@ -49,6 +60,7 @@ struct BwdParams {
   int n_blocks;
   float c2;     // scale * log2(e)
   float scale;
+  SeqOrder order;  // varlen only
 };
 
 constexpr int kFwdBlockM = 256;   // query rows per forward workgroup (8 waves x 32)
