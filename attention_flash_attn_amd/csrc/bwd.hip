@@ -200,6 +200,25 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   bool kvalid = key < nk;
   if (kvalid && sl.mask) kvalid = sl.mask[key] != 0;
   const uint64_t kball = __ballot(kvalid);
+  if (!__syncthreads_or(kvalid)) {
+    // Every key of the workgroup is masked: dK = dV = 0 without the query loop (added to
+    // nothing when accumulating).
+    if (sub == 0 && key < nk && !(ACC && (p.acc_flags & 2))) {
+      const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * hl;
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const long o = off + 8 * c;
+        if (ACC) {
+          *reinterpret_cast<f32x4*>(p.dk_acc + o) = f32x4{};
+          *reinterpret_cast<f32x4*>(p.dv_acc + o) = f32x4{};
+        } else {
+          *reinterpret_cast<bf16x4*>(p.dk + o) = to_bf16x4(f32x4{});
+          *reinterpret_cast<bf16x4*>(p.dv + o) = to_bf16x4(f32x4{});
+        }
+      }
+    }
+    return;
+  }
 
   int qoff[NKS], troff[NMB][2];
 #pragma unroll
@@ -537,7 +556,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     if (more) {
       vw_next = kv.word((j + 1) * BN, mbytes);
       mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
-      issue((j + 1) * BN, nk_, nv);
+      if (vw_next != 0) issue((j + 1) * BN, nk_, nv);  // a fully masked tile is not read
     }
     if (vw != 0) compute(ck, cv, j * BN, vw);
     wait_tile_loads();
