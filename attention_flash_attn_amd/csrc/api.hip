@@ -21,6 +21,9 @@ bool head_dim_ok(int D) { return D == 64 || D == 128; }
 // The backward starts its score accumulators from -LSE/scale; the lower bound keeps that
 // finite for any LSE the forward can produce.
 bool scale_ok(float s) { return isfinite(s) && s >= 0x1p-64f; }
+// Tile copies address up to 256 rows of one tensor (row stride H * D elements) with 32-bit
+// signed byte offsets.
+bool row_width_ok(int H, int D) { return 256L * 2 * H * D <= INT_MAX; }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 // A tensor pointer may be NULL only when the tensor has no elements.
@@ -30,7 +33,7 @@ bool missing(const void* ptr, bool has_elements) { return ptr == nullptr && has_
 int check_dense(int B, int Sq, int Sk, int H, int D, float scale) {
   if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || D < 0) return ATTN_ERR_SHAPE;
   if (!scale_ok(scale)) return ATTN_ERR_SHAPE;
-  if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_ok(D) || !row_width_ok(H, D)) return ATTN_ERR_UNSUPPORTED;
   // Row indices (b*S + s) and workgroup counts are kept in 32-bit integers.
   if ((long)B * Sq > INT_MAX || (long)B * Sk > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   if ((cdiv(Sq, 32) + cdiv(Sk, 32)) * H * (long)B > INT_MAX)
@@ -50,7 +53,7 @@ int check_kv_heads(int H, int Hk) {
 int check_varlen(int nseq, const int32_t* cu, int H, int D, float scale, int* T, int* maxlen) {
   if (nseq < 0 || H < 0 || D < 0) return ATTN_ERR_SHAPE;
   if (!scale_ok(scale)) return ATTN_ERR_SHAPE;
-  if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_ok(D) || !row_width_ok(H, D)) return ATTN_ERR_UNSUPPORTED;
   if (cu[0] != 0) return ATTN_ERR_SEQLENS;
   int mx = 0;
   for (int n = 0; n < nseq; ++n) {
@@ -220,7 +223,7 @@ static BwdParams bwd_params(int B, int Sq, int Sk, int H, int Hk, float scale, c
 
 // Grid of the backward launch: per (outer, key/value head) the dQ workgroups of its G query
 // heads and its dK/dV workgroups; the kernel starts every workgroup of the longer kind
-// before the shorter ones.  Work per workgroup: dK/dV 128 keys x G * nq query rows x 4
+// before the shorter ones.  Work per workgroup: dK/dV 256 keys x G * nq query rows x 4
 // products, dQ 256 query rows x nk keys x 3 products.
 static void bwd_grid(BwdParams& p, int nq, int nk, int outer) {
   p.n_kv_tiles = (int)cdiv(nk, attn::kDkvBlockN);

@@ -14,13 +14,12 @@
 // dK/dV and dQ come from two kernels that each own their output rows, so
 // there are no atomics and the result is bitwise reproducible.
 //
-// dK/dV workgroup: 8 waves, 128 keys.  The keys' K and V rows sit in LDS for the whole
-// loop; query tiles of 64 rows (Q, dO, LSE, delta) are double-buffered in LDS, filled
-// asynchronously by buffer loads into XOR-swizzled LDS rows (tile.hpp).  Wave w owns key
-// block w%4 (32 keys, one per lane of the score tile S = Q K^T) and query sub-tile w/4 of
-// every tile, with its dK^T, dV^T accumulators in registers across the loop; the two
-// waves of a key block add their partial sums through LDS at the end.  Q^T and dO^T
-// operands come from the LDS transposing read.
+// dK/dV workgroup: 8 waves, 256 keys.  The keys' K rows go to registers and their V rows
+// sit in LDS for the whole loop; query tiles of 64 rows (Q, dO, LSE, delta) are
+// double-buffered in LDS, filled asynchronously by buffer loads into XOR-swizzled LDS
+// rows (tile.hpp).  Wave w owns key block w (32 keys, one per lane of the score tile
+// S = Q K^T) and both 32-row halves of every tile, with its dK^T, dV^T accumulators in
+// registers across the loop.  Q^T and dO^T operands come from the LDS transposing read.
 //
 // dQ workgroup: 8 waves, 256 query rows; each wave keeps its 32 rows of Q and dO (B
 // operands of S^T = K Q^T and dP^T = V dO^T: one query per lane, so LSE and delta are
@@ -139,14 +138,14 @@ __device__ __forceinline__ f32x16 row_values16(const float* p) {
 
 template <int D>
 struct DkdvSmem {
-  static constexpr int BN = 128;  // keys per workgroup: 4 blocks of 32
+  static constexpr int BN = 256;  // keys per workgroup: 8 blocks of 32, one per wave
   static constexpr int BQ = 64;   // query rows per staged tile: 2 sub-tiles of 32
   // The Q/dO tiles come first: LDS reads address at most 64 KB past a register, so with
   // all four of them in the first 64 KB one set of per-lane offsets serves every buffer.
+  // Before the loop the same 64 KB stage the workgroup's K rows on their way to registers.
   char q[2][BQ * 2 * D];          // double-buffered Q and dO tiles
   char o[2][BQ * 2 * D];
-  char k[BN * 2 * D];             // K and V of the workgroup's keys, loaded once
-  char v[BN * 2 * D];
+  char v[BN * 2 * D];             // V of the workgroup's keys, loaded once
   float l[2][BQ];                 // LSE * log2(e) and delta of the tile's rows
   float d[2][BQ];
 };
@@ -172,22 +171,23 @@ __device__ __forceinline__ void perm_tr_offsets(int lane, int (&off)[D / 32][2])
                                      32 * mb + 16 * (g & 1) + 4 * (src & 3));
 }
 
-// dK/dV: 8 waves, 128 keys.  Wave w owns key block w%4 (32 keys, one per lane) and
-// query sub-tile w/4 of every 64-row tile, so two waves accumulate partial dK/dV for
-// the same keys; they are summed through LDS at the end.  The wave's K fragments (the B
-// operand of S = Q K^T, 32 registers) are read from LDS once and kept in registers for the
-// whole loop; V stays in LDS, which keeps a wave within 256 registers: two waves per SIMD,
-// so one wave's MFMAs run while the other does its softmax VALU work.
+// dK/dV: 8 waves, 256 keys.  Wave w owns key block w (32 keys, one per lane) and both
+// 32-row halves of every 64-row query tile, so each staged tile feeds 64 MFMAs per wave
+// and no two waves share a key.  The wave's K fragments (the B operand of S = Q K^T, 32
+// registers) are read from LDS once and kept in registers for the whole loop; V stays in
+// LDS, which keeps a wave within 256 registers: two waves per SIMD, so one wave's MFMAs
+// run while the other does its softmax VALU work.
 template <int D, bool VARLEN, bool ACC>
 __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, DkdvSmem<D>& sm) {
   constexpr int BN = DkdvSmem<D>::BN, BQ = DkdvSmem<D>::BQ, NW = 8;
   constexpr int RB = 2 * D;
   constexpr int NKS = D / 16, NMB = D / 32;
+  static_assert(sizeof(sm.q) + sizeof(sm.o) == BN * RB && offsetof(DkdvSmem<D>, q) == 0,
+                "the Q/dO buffers stage K");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int hl = lane >> 5, l32 = lane & 31;
-  const int kblk = wave & 3, sub = wave >> 2;
   const int kb0 = sl.tile * BN;
   if (kb0 >= sl.nk) return;  // block-uniform
   // Q/dO rows hold H heads, K/V/dK/dV rows Hk.  The loop runs over the query tiles of all
@@ -196,14 +196,14 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int nq = sl.nq, nk = sl.nk;
 
-  const int key = kb0 + 32 * kblk + l32;
+  const int key = kb0 + 32 * wave + l32;
   bool kvalid = key < nk;
   if (kvalid && sl.mask) kvalid = sl.mask[key] != 0;
   const uint64_t kball = __ballot(kvalid);
   if (!__syncthreads_or(kvalid)) {
     // Every key of the workgroup is masked: dK = dV = 0 without the query loop (added to
     // nothing when accumulating).
-    if (sub == 0 && key < nk && !(ACC && (p.acc_flags & 2))) {
+    if (key < nk && !(ACC && (p.acc_flags & 2))) {
       const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * hl;
 #pragma unroll
       for (int c = 0; c < D / 8; ++c) {
@@ -231,10 +231,11 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.qhead * D;
   const bf16* obase = p.dout + (long)sl.qrow0 * rs + (long)sl.qhead * D;
+  char* kstage = reinterpret_cast<char*>(&sm);
   {
     TileLoader<D, BN, NW> kvld;
     kvld.init(rsk, same_row);
-    kvld.issue(sm.k, kbase, rsk, kb0, nk, same_row);
+    kvld.issue(kstage, kbase, rsk, kb0, nk, same_row);
     kvld.issue(sm.v, vbase, rsk, kb0, nk, same_row);
   }
   TileLoader<D, BQ, 4> ld;  // used by waves 0..3
@@ -255,10 +256,10 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     const long qi = sl.lse_base + (long)i * p.Sq + min(q0 + lane, nq - 1);
     lraw = p.lse[qi];
     draw = p.delta[qi];
-    // Only the sub-tile-0 waves copy: right after the barrier the copies queue up in the
-    // memory pipeline and stall the waves that issue them (32 KB at ~64 B/clock), and
-    // meanwhile the sub-tile-1 wave of each SIMD has its matrix unit to itself.
-    if (sub == 0) {
+    // Only waves 0..3 copy: right after the barrier the copies queue up in the memory
+    // pipeline and stall the waves that issue them (32 KB at ~64 B/clock), and meanwhile
+    // the other wave of each SIMD has its matrix unit to itself.
+    if (wave < 4) {
       ld.issue(qt, qbase + (long)i * D, rs, q0, nq, qrow_of);
       ld.issue(ot, obase + (long)i * D, rs, q0, nq, qrow_of);
     }
@@ -280,27 +281,28 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
   const float c2 = p.c2;
-  const int qr = sub * 32 * RB, kr = kblk * 32 * RB;
+  const int kr = wave * 32 * RB;
   bf16x8 kreg[NKS];  // this wave's 32 keys as the B operand of S = Q K^T, one per ks
 
-  // One 32x32 (query x key) step: scores S = Q K^T and dP = dO V^T (one key per lane),
-  // weights P = exp(scale S - LSE) and dS = P (dP - delta), then dV^T += dO^T P and
-  // dK^T += Q^T dS.  The S and dP accumulators start from their rows' -LSE/scale and
-  // -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in registers.
-  // No key-mask work here: with one key per lane, P and dS of an excluded key only reach
-  // that key's own accumulators, which are stored as zeros.  Causal tiles on the diagonal
-  // zero P per element in a branch taken only there.
-  auto compute = [&](const char* kt, const char* vt, const char* qt, const char* ot,
-                     const float* lt, const float* dt, int q0) {
-    // Register r holds query 32*sub + 16*(r/8) + 8*hl + r%8 of the tile.
-    f32x16 s = row_values16(lt + 32 * sub + 8 * hl), dp = row_values16(dt + 32 * sub + 8 * hl);
+  // One 32x32 (query x key) step on half u of the tile: scores S = Q K^T and dP = dO V^T
+  // (one key per lane), weights P = exp(scale S - LSE) and dS = P (dP - delta), then
+  // dV^T += dO^T P and dK^T += Q^T dS.  The S and dP accumulators start from their rows'
+  // -LSE/scale and -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in
+  // registers.  No key-mask work here: with one key per lane, P and dS of an excluded key
+  // only reach that key's own accumulators, which are stored as zeros.  Causal blocks that
+  // hold a key after one of their rows zero P per element in a branch taken only there.
+  auto compute = [&](const char* vt, const char* qt, const char* ot, const float* lt,
+                     const float* dt, int q0, int u) {
+    const int qr = u * 32 * RB;
+    // Register r holds query 32*u + 16*(r/8) + 8*hl + r%8 of the tile.
+    f32x16 s = row_values16(lt + 32 * u + 8 * hl), dp = row_values16(dt + 32 * u + 8 * hl);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       s = mfma32(lds_row16(qt, qr + qoff[ks]), kreg[ks], s);
-    if (p.causal && q0 < kb0 + BN - 1) {
+    if (p.causal && q0 + 32 * u < kb0 + 32 * wave + 31) {
       keep_branch();
-      // A tile on the diagonal: P = 0 where this lane's key comes after register r's row.
-      const int first = key - q0 - 32 * sub - 8 * hl;  // row offset below which P = 0
+      // P = 0 where this lane's key comes after register r's row.
+      const int first = key - q0 - 32 * u - 8 * hl;  // row offset below which P = 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 16 * (r >> 3) + (r & 7) >= first ? s[r] : -INFINITY;
     }
@@ -327,46 +329,42 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   // All tile buffers are distinct __restrict__ parameters, so once inlined the compiler
   // can tell reads of the current tile from the asynchronous copy into the next one
   // (without that it waits for the copy before the first LDS read).
-  auto step = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt,
-                  const char* __restrict__ cq, const char* __restrict__ co,
-                  const float* __restrict__ cl, const float* __restrict__ cd, char* __restrict__ nq_,
-                  char* __restrict__ no_, float* __restrict__ nl, float* __restrict__ nd) {
+  auto step = [&](int j, const char* __restrict__ vt, const char* __restrict__ cq,
+                  const char* __restrict__ co, const float* __restrict__ cl,
+                  const float* __restrict__ cd, char* __restrict__ nq_, char* __restrict__ no_,
+                  float* __restrict__ nl, float* __restrict__ nd) {
     const bool more = j + 1 < ntiles;
     if (more) issue(j + 1, nq_, no_);
-    if (kball != 0) compute(kt, vt, cq, co, cl, cd, tile_q0(j));
+    if (kball != 0) {
+      const int q0 = tile_q0(j);
+      compute(vt, cq, co, cl, cd, q0, 0);
+      compute(vt, cq, co, cl, cd, q0, 1);
+    }
     if (more) publish_stats(j + 1, nl, nd);
     wait_tile_loads();
     __syncthreads();
   };
+  // K: staged, read into registers, then its staging space is handed to the Q/dO tiles
+  // (the LDS reads must have returned before the barrier lets the copies in).
+  wait_tile_loads();
+  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) kreg[ks] = lds_row16(kstage, kr + qoff[ks]);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
   if (ntiles > 0) {
     issue(0, sm.q[0], sm.o[0]);
     publish_stats(0, sm.l[0], sm.d[0]);
   }
   wait_tile_loads();
   __syncthreads();
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) kreg[ks] = lds_row16(sm.k, kr + qoff[ks]);
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, sm.k, sm.v, sm.q[0], sm.o[0], sm.l[0], sm.d[0], sm.q[1], sm.o[1], sm.l[1], sm.d[1]);
+    step(j, sm.v, sm.q[0], sm.o[0], sm.l[0], sm.d[0], sm.q[1], sm.o[1], sm.l[1], sm.d[1]);
     if (j + 1 < ntiles)
-      step(j + 1, sm.k, sm.v, sm.q[1], sm.o[1], sm.l[1], sm.d[1], sm.q[0], sm.o[0], sm.l[0], sm.d[0]);
+      step(j + 1, sm.v, sm.q[1], sm.o[1], sm.l[1], sm.d[1], sm.q[0], sm.o[0], sm.l[0], sm.d[0]);
   }
 
-  // Sum the two query halves: waves of sub-tile 1 park their accumulators in LDS (the
-  // tile buffers are free now), waves of sub-tile 0 add them and store.
-  static_assert(2 * 4 * NMB * 16 * 64 * sizeof(float) <= sizeof(DkdvSmem<D>), "reduction space");
-  float* red = reinterpret_cast<float*>(&sm);
-  if (sub == 1) {
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red[((kblk * NMB + mb) * 16 + r) * 64 + lane] = dkacc[mb][r];
-        red[(((4 + kblk) * NMB + mb) * 16 + r) * 64 + lane] = dvacc[mb][r];
-      }
-  }
-  __syncthreads();
-  if (sub == 0 && key < nk) {
+  if (key < nk) {
     const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * hl;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -376,10 +374,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j4 + e;
-          const float dkv = dkacc[mb][r] + red[((kblk * NMB + mb) * 16 + r) * 64 + lane];
-          const float dvv = dvacc[mb][r] + red[(((4 + kblk) * NMB + mb) * 16 + r) * 64 + lane];
-          a[e] = kvalid ? dkv * p.scale : 0.f;
-          b[e] = kvalid ? dvv : 0.f;
+          a[e] = kvalid ? dkacc[mb][r] * p.scale : 0.f;
+          b[e] = kvalid ? dvacc[mb][r] : 0.f;
         }
         const long o = off + 32 * mb + 8 * j4;
         if (ACC) {

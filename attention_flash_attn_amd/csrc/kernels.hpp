@@ -65,7 +65,7 @@ struct BwdParams {
 
 constexpr int kFwdBlockM = 256;   // query rows per forward workgroup (8 waves x 32)
 constexpr int kDqBlockM = 256;    // query rows per dQ workgroup
-constexpr int kDkvBlockN = 128;   // key rows per dK/dV workgroup
+constexpr int kDkvBlockN = 256;   // key rows per dK/dV workgroup
 
 hipError_t launch_fwd(int D, bool varlen, const FwdParams& p, hipStream_t stream);
 // accum: fp32 dQ/dK/dV into p.dq_acc/dk_acc/dv_acc (added or overwritten per p.acc_flags)

@@ -56,7 +56,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size is negative, or scale is not finite and >= 2^-64 */
-  ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, or a size beyond the index range */
+  ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, H * D > 2^22, or a size beyond the
+                               index range */
   ATTN_ERR_SEQLENS = 4,     /* cu_seqlens is not 0 = c0 <= c1 <= ... <= c_nseq = T */
   ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
 } attn_status;

@@ -68,6 +68,9 @@ def test_fwd_validation(L):
     for D in (0, 32, 96, 256):
         assert fwd(L, D=D) == UNSUP
     assert fwd(L, B=2, Sq=2 ** 30 + 1) == UNSUP
+    # rows wider than 2^22 elements (H * D): tile copies use 32-bit byte offsets
+    assert fwd(L, H=2 ** 15, D=128) == UNSUP
+    assert fwd(L, H=2 ** 16, D=64) == UNSUP
     # zero-sized problems succeed without launching anything
     assert fwd(L, B=0) == OK
     assert fwd(L, Sq=0) == OK
@@ -176,6 +179,7 @@ def test_varlen_validation(L):
     assert call([1, 5, 9]) == (SEQ, SEQ)        # must start at 0
     assert call([0, 5, 4]) == (SEQ, SEQ)        # must not decrease
     assert call([0, 5, 9], D=72) == (UNSUP, UNSUP)
+    assert call([0, 5, 9], H=2 ** 15) == (UNSUP, UNSUP)
     assert call([0, 5, 9], nseq=-1) == (SHAPE, SHAPE)
     assert call([0]) == (OK, OK)                # no sequences: nothing to do
     assert call([0, 0, 0]) == (OK, OK)          # empty sequences: T = 0

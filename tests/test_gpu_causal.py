@@ -4,7 +4,7 @@ through the C ABI against the fp64 oracle's causal mode on the same seeded bf16 
 
 The kernels skip key tiles past a workgroup's last query row and mask per element only on
 the tiles that cross the diagonal, so the cases put the diagonal inside and across tiles
-(64-key forward/dQ tiles, 128-key dK/dV blocks, 128/256-row query tiles), with ragged
+(64-key forward/dQ tiles, 256-key dK/dV blocks, 128/256-row query tiles), with ragged
 tails, Sq != Sk both ways, key masks (rows whose visible keys are all masked get out = 0,
 LSE = -inf), grouped-query heads and packed sequences.
 """
