@@ -6,6 +6,8 @@
 #include <math.h>
 #include <limits.h>
 
+#include <algorithm>
+
 #include "libattn.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -224,12 +226,18 @@ static BwdParams bwd_params(int B, int Sq, int Sk, int H, int Hk, float scale, c
 // Grid of the backward launch: per (outer, key/value head) the dQ workgroups of its G query
 // heads and its dK/dV workgroups; the kernel starts every workgroup of the longer kind
 // before the shorter ones.  Work per workgroup: dK/dV 256 keys x G * nq query rows x 4
-// products, dQ 256 query rows x nk keys x 3 products.
-static void bwd_grid(BwdParams& p, int nq, int nk, int outer) {
+// products, dQ 256 query rows x nk keys x 3 products.  When the dQ workgroups come last
+// and all take equally long (dense, non-causal), the last half-CU-count of them run as
+// split workgroups (two per tile, 128 rows each, half the time), so that the launch's last
+// round finishes together instead of leaving most CUs idle behind a few whole tiles.
+static void bwd_grid(BwdParams& p, int nq, int nk, int outer, bool may_split, hipStream_t stream) {
   p.n_kv_tiles = (int)cdiv(nk, attn::kDkvBlockN);
   p.n_q_tiles = (int)cdiv(nq, attn::kDqBlockM);
   p.dkdv_first = (long)attn::kDkvBlockN * 4 * p.G * nq > (long)attn::kDqBlockM * 3 * nk;
-  p.n_blocks = (p.n_kv_tiles + p.G * p.n_q_tiles) * p.Hk * outer;
+  const int n_q_all = p.G * p.n_q_tiles * p.Hk * outer;
+  p.n_q_split = 0;
+  if (may_split && (p.G > 1 || p.dkdv_first)) p.n_q_split = std::min(n_q_all, cu_count(stream) / 2);
+  p.n_blocks = (p.n_kv_tiles + p.G * p.n_q_tiles) * p.Hk * outer + p.n_q_split;
 }
 
 int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
@@ -264,7 +272,7 @@ int attn_bwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int fl
   BwdParams p = bwd_params(B, Sq, Sk, H, Hk, scale, q, k, v, key_mask, lse, delta, dout, dq, dk,
                            dv, nullptr);
   p.causal = flags & ATTN_CAUSAL;
-  bwd_grid(p, Sq, Sk, B);
+  bwd_grid(p, Sq, Sk, B, !p.causal, s);
   return status_of(attn::launch_bwd(D, false, false, p, s));
 }
 
@@ -287,7 +295,7 @@ int attn_bwd_accum(int B, int Sq, int Sk, int H, int D, float scale, const void*
   p.dk_acc = dk_acc;
   p.dv_acc = dv_acc;
   p.acc_flags = flags;
-  bwd_grid(p, Sq, Sk, B);
+  bwd_grid(p, Sq, Sk, B, true, static_cast<hipStream_t>(stream));
   return status_of(attn::launch_bwd(D, false, true, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -393,7 +401,7 @@ int attn_varlen_bwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
                            dv, cu_seqlens_dev);
   p.causal = flags & ATTN_CAUSAL;
   p.order = seq_order(nseq, cu_seqlens_host);
-  bwd_grid(p, maxlen, maxlen, nseq);
+  bwd_grid(p, maxlen, maxlen, nseq, false, s);
   return status_of(attn::launch_bwd(D, true, false, p, s));
 }
 

@@ -30,12 +30,10 @@
 // matrix instructions run while the other does its exponentials and conversions (a wave
 // does not overlap the two itself).
 //
-// Both run in ONE launch: the grid is grouped per (batch|sequence, key/value head), each
-// group holding the dQ workgroups of its query heads and its dK/dV workgroups (the longer
-// kind first), and groups
-// are dealt to XCDs in contiguous ranges.  Every XCD therefore gets the same mix
-// of the two workgroup kinds, and the two kinds of one head share its Q/K/V/dO
-// in that XCD's L2.
+// Both run in ONE launch: every workgroup of the longer kind first, in plain block order
+// (dealt round-robin to the XCDs, so each XCD gets its share of both kinds), and in dense
+// non-causal launches the last dQ tiles as split workgroups of half the rows, so that the
+// launch's last round ends together (bwd_kernel).
 //
 // Partial tiles (a ragged tail, a mask edge) zero the excluded weights in a
 // branch taken only there, so full tiles carry no per-element mask work.
@@ -220,10 +218,28 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     return;
   }
 
+  // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
+  // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
+  // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt before every use from the
+  // step-0 offsets, which keeps 14 registers free for the loop.
+  int qoff0 = tile_off<D>(l32, hl), tr0[2];
+  {
+    int t[NMB][2];
+    perm_tr_offsets<D>(lane, t);
+    tr0[0] = t[0][0];
+    tr0[1] = t[0][1];
+  }
   int qoff[NKS], troff[NMB][2];
+  auto offsets = [&]() {
+    asm volatile("" : "+v"(qoff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qoff[ks] = tile_off<D>(l32, 2 * ks + hl);
-  perm_tr_offsets<D>(lane, troff);
+    for (int ks = 0; ks < NKS; ++ks) qoff[ks] = qoff0 ^ (32 * ks);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      troff[mb][0] = tr0[0] ^ (64 * mb);
+      troff[mb][1] = tr0[1] ^ (64 * mb);
+    }
+  };
 
   auto same_row = [](int r) { return r; };
   auto qrow_of = [](int r) { return perm32_row(r); };
@@ -284,18 +300,31 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   const int kr = wave * 32 * RB;
   bf16x8 kreg[NKS];  // this wave's 32 keys as the B operand of S = Q K^T, one per ks
 
-  // One 32x32 (query x key) step on half u of the tile: scores S = Q K^T and dP = dO V^T
-  // (one key per lane), weights P = exp(scale S - LSE) and dS = P (dP - delta), then
+  // dP = dO V^T of both 32-row halves of a tile (one key per lane), so that each V fragment
+  // read feeds two MFMAs.  The accumulators start from their rows' -delta.
+  auto scores_dp = [&](const char* vt, const char* ot, const float* dt, f32x16& dp0, f32x16& dp1) {
+    offsets();
+    dp0 = row_values16(dt + 8 * hl);
+    dp1 = row_values16(dt + 32 + 8 * hl);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 vf = lds_row16(vt, kr + qoff[ks]);
+      dp0 = mfma32(lds_row16(ot, qoff[ks]), vf, dp0);
+      dp1 = mfma32(lds_row16(ot, 32 * RB + qoff[ks]), vf, dp1);
+    }
+  };
+  // One 32x32 (query x key) step on half u of the tile, given its dP: scores S = Q K^T (one
+  // key per lane), weights P = exp(scale S - LSE) and dS = P (dP - delta), then
   // dV^T += dO^T P and dK^T += Q^T dS.  The S and dP accumulators start from their rows'
   // -LSE/scale and -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in
   // registers.  No key-mask work here: with one key per lane, P and dS of an excluded key
   // only reach that key's own accumulators, which are stored as zeros.  Causal blocks that
   // hold a key after one of their rows zero P per element in a branch taken only there.
-  auto compute = [&](const char* vt, const char* qt, const char* ot, const float* lt,
-                     const float* dt, int q0, int u) {
+  auto compute = [&](const char* qt, const char* ot, const float* lt, int q0, int u, f32x16 dp) {
     const int qr = u * 32 * RB;
+    offsets();
     // Register r holds query 32*u + 16*(r/8) + 8*hl + r%8 of the tile.
-    f32x16 s = row_values16(lt + 32 * u + 8 * hl), dp = row_values16(dt + 32 * u + 8 * hl);
+    f32x16 s = row_values16(lt + 32 * u + 8 * hl);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       s = mfma32(lds_row16(qt, qr + qoff[ks]), kreg[ks], s);
@@ -306,9 +335,6 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 16 * (r >> 3) + (r & 7) >= first ? s[r] : -INFINITY;
     }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      dp = mfma32(lds_row16(ot, qr + qoff[ks]), lds_row16(vt, kr + qoff[ks]), dp);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s[r] = __builtin_amdgcn_exp2f(s[r] * c2);
@@ -337,8 +363,10 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     if (more) issue(j + 1, nq_, no_);
     if (kball != 0) {
       const int q0 = tile_q0(j);
-      compute(vt, cq, co, cl, cd, q0, 0);
-      compute(vt, cq, co, cl, cd, q0, 1);
+      f32x16 dp0, dp1;
+      scores_dp(vt, co, cd, dp0, dp1);
+      compute(cq, co, cl, q0, 0, dp0);
+      compute(cq, co, cl, q0, 1, dp1);
     }
     if (more) publish_stats(j + 1, nl, nd);
     wait_tile_loads();
@@ -348,6 +376,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   // (the LDS reads must have returned before the barrier lets the copies in).
   wait_tile_loads();
   __syncthreads();
+  offsets();
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) kreg[ks] = lds_row16(kstage, kr + qoff[ks]);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -397,23 +426,32 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 
 // ------------------------------------------------------------------ dQ
 
+// half < 0: a whole workgroup, 256 query rows.  half = 0 or 1: a split workgroup, the
+// 128-row half `half` of the tile, whose wave groups (waves 0..3 and 4..7, the same 128
+// rows) each take one half of the key tiles with their own double-buffered K/V tiles in
+// sm[group], and whose partial dQ sums are added through LDS at the end.  Split
+// workgroups finish a launch's last round in half the time (dense non-causal grids only).
 template <int D, bool VARLEN, bool ACC>
-__device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqSmem<D>& sm) {
-  constexpr int BM = 256, BN = DqSmem<D>::BN, NW = 8;
+__device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqSmem<D> (&sm)[2],
+                                         int half) {
+  constexpr int BM = 256, BN = DqSmem<D>::BN;
   constexpr int RB = 2 * D;
   constexpr int NKS = D / 16, NMB = D / 32;
+  constexpr int GB = sizeof(DqSmem<D>);  // LDS distance between the wave groups' tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int hl = lane >> 5, l32 = lane & 31;
+  const bool split = half >= 0;
+  const int grp = split ? wave >> 2 : 0;
   // Causal: the last query tiles see the most keys, so they are dealt out first.
-  const int qb = (p.causal ? p.n_q_tiles - 1 - sl.tile : sl.tile) * BM;
+  const int qb = (p.causal ? p.n_q_tiles - 1 - sl.tile : sl.tile) * BM + (split ? half * (BM / 2) : 0);
   if (qb >= sl.nq) return;  // block-uniform
   // Q/dO/dQ rows hold H heads, K/V rows Hk (this query head reads key/value head kvhead).
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int nq = sl.nq, nk = sl.nk;
 
-  const int qrow = qb + wave * 32 + l32;
+  const int qrow = qb + (split ? wave & 3 : wave) * 32 + l32;
   bf16x8 qreg[NKS], doreg[NKS];
   {
     const long off = ((long)sl.qrow0 + min(qrow, nq - 1)) * rs + (long)sl.qhead * D + 8 * hl;
@@ -432,13 +470,15 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
   // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
   // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt at every step from the step-0
-  // offsets, which keeps 14 registers free for the loop.
-  int koff0 = tile_off<D>(l32, hl), tr0[2];
+  // offsets, which keeps 14 registers free for the loop.  The offsets also carry the wave
+  // group's distance to its own tiles (GB, a multiple of 256 bytes, which the XORs leave
+  // alone), so the tile addresses stay constants.
+  int koff0 = tile_off<D>(l32, hl) + grp * GB, tr0[2];
   {
     int troff[NMB][2];
     perm_tr_offsets<D>(lane, troff);
-    tr0[0] = troff[0][0];
-    tr0[1] = troff[0][1];
+    tr0[0] = troff[0][0] + grp * GB;
+    tr0[1] = troff[0][1] + grp * GB;
   }
   int koff[NKS], troff[NMB][2];
   auto offsets = [&]() {
@@ -455,14 +495,14 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const bf16* kbase = p.k + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   auto krow_of = [](int r) { return perm32_row(r); };
-  TileLoader<D, BN, 4> ld;  // used by waves 0..3
-  ld.init(rsk, krow_of);
+  TileLoader<D, BN, 4> ld;  // used by waves 0..3 (split: each group's four waves)
+  ld.init(rsk, krow_of, 4 * grp);
   // Only waves 0..3 copy (see dkdv_block): while they stall at issue, waves 4..7, one per
-  // SIMD, keep the matrix units busy.
+  // SIMD, keep the matrix units busy.  In a split workgroup each group copies its own tiles.
   auto issue = [&](int k0, char* kt, char* vt) {
-    if (wave < 4) {
-      ld.issue(kt, kbase, rsk, k0, nk, krow_of);
-      ld.issue(vt, vbase, rsk, k0, nk, krow_of);
+    if (split || wave < 4) {
+      ld.issue(kt + grp * GB, kbase, rsk, k0, nk, krow_of);
+      ld.issue(vt + grp * GB, vbase, rsk, k0, nk, krow_of);
     }
   };
 
@@ -541,34 +581,56 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   // Causal: keys past the workgroup's last query row are never seen.
   const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
   const int ntiles = (kend + BN - 1) / BN;
+  // This wave group's key tiles [t0, t1), hn steps (a split workgroup's groups step in
+  // lockstep, one barrier per step; a group past its last tile only takes the barriers).
+  const int hn = split ? (ntiles + 1) / 2 : ntiles;
+  const int t0 = grp * hn, t1 = min(ntiles, t0 + hn);
   uint64_t vw = 0;
   const KeyValidity kv{sl.mask, nk};
   uint32_t mbytes = 0;  // raw mask bytes of tile j + 1 during step j
   // Current and next tile buffers as distinct __restrict__ parameters (see dkdv_block).
   auto step = [&](int j, const char* __restrict__ ck, const char* __restrict__ cv,
                   char* __restrict__ nk_, char* __restrict__ nv) {
-    const bool more = j + 1 < ntiles;
+    const bool more = j + 1 < t1;
     uint64_t vw_next = 0;
     if (more) {
       vw_next = kv.word((j + 1) * BN, mbytes);
       mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
       if (vw_next != 0) issue((j + 1) * BN, nk_, nv);  // a fully masked tile is not read
     }
-    if (vw != 0) compute(ck, cv, j * BN, vw);
+    if (j < t1 && vw != 0) compute(ck, cv, j * BN, vw);
     wait_tile_loads();
     __syncthreads();
     vw = vw_next;
   };
-  if (ntiles > 0) {
-    vw = kv.word(0, kv.load(0));
-    mbytes = kv.load(BN);
-    issue(0, sm.k[0], sm.v[0]);
+  if (t0 < t1) {
+    vw = kv.word(t0 * BN, kv.load(t0 * BN));
+    mbytes = kv.load((t0 + 1) * BN);
+    issue(t0 * BN, sm[0].k[0], sm[0].v[0]);
     wait_tile_loads();
   }
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, sm.k[0], sm.v[0], sm.k[1], sm.v[1]);
-    if (j + 1 < ntiles) step(j + 1, sm.k[1], sm.v[1], sm.k[0], sm.v[0]);
+  for (int s = 0; s < hn; s += 2) {
+    step(t0 + s, sm[0].k[0], sm[0].v[0], sm[0].k[1], sm[0].v[1]);
+    if (s + 1 < hn) step(t0 + s + 1, sm[0].k[1], sm[0].v[1], sm[0].k[0], sm[0].v[0]);
+  }
+  if (split) {
+    // Group 1 parks its partial sums in LDS (every tile read has completed at the last
+    // step's barrier), group 0 adds them and stores.
+    static_assert(4 * NMB * 16 * 64 * sizeof(float) <= 2 * sizeof(DqSmem<D>), "reduction space");
+    float* red = reinterpret_cast<float*>(&sm[0]) + (wave & 3) * (NMB * 16 * 64);
+    if (grp == 1) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(mb * 16 + r) * 64 + lane] = dqacc[mb][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[mb][r] += red[(mb * 16 + r) * 64 + lane];
   }
 
   if (qrow < nq) {
@@ -604,17 +666,26 @@ template <int D, bool VARLEN, bool ACC>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   union Smem {
     DkdvSmem<D> kv;
-    DqSmem<D> q;
+    DqSmem<D> q[2];  // [1]: the second wave group's tiles of a split dQ workgroup
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int nqw = p.G * p.n_q_tiles;
   const int per_group = p.n_kv_tiles + nqw;
-  const int ngroups = p.n_blocks / per_group;
+  const int ngroups = (p.n_blocks - p.n_q_split) / per_group;
   const int n_kv_all = p.n_kv_tiles * ngroups, n_q_all = nqw * ngroups;
+  const int n_q_blocks = n_q_all + p.n_q_split;  // split dQ tiles count twice
   const int L = blockIdx.x;
   const bool kv_first = p.G > 1 || p.dkdv_first;
-  const bool kv = kv_first ? L < n_kv_all : L >= n_q_all;
-  const int r = kv ? (kv_first ? L : L - n_q_all) : (kv_first ? L - n_kv_all : L);
+  const bool kv = kv_first ? L < n_kv_all : L >= n_q_blocks;
+  int r = kv ? (kv_first ? L : L - n_q_blocks) : (kv_first ? L - n_kv_all : L);
+  // The last n_q_split dQ tiles of the grid (host-chosen: dense non-causal launches whose
+  // dQ workgroups come last) run as two split workgroups each, one per 128-row half.
+  int half = -1;
+  if (!kv && r >= n_q_all - p.n_q_split) {
+    const int b = r - (n_q_all - p.n_q_split);
+    r = n_q_all - p.n_q_split + b / 2;
+    half = b & 1;
+  }
   int group, idx;
   if (p.causal) {
     // Causal workgroups differ in length by tile (dK/dV: the first key tiles, dQ: the last
@@ -637,7 +708,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
   if (kv)
     dkdv_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, idx, 0), sm.kv);
   else
-    dq_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, idx % p.n_q_tiles, idx / p.n_q_tiles), sm.q);
+    dq_block<D, VARLEN, ACC>(p, decode<VARLEN>(p, group, idx % p.n_q_tiles, idx / p.n_q_tiles), sm.q,
+                             half);
 }
 
 template <int D, bool VARLEN, bool ACC>

@@ -57,6 +57,7 @@ struct BwdParams {
   int n_kv_tiles;  // dK/dV workgroups per (outer, key/value head)
   int n_q_tiles;   // dQ workgroups per (outer, query head)
   int dkdv_first;  // grid order: the dK/dV workgroups first (they are the longer kind)
+  int n_q_split;   // the last dQ tiles of the grid that run as two half-row workgroups each
   int n_blocks;
   float c2;     // scale * log2(e)
   float scale;
