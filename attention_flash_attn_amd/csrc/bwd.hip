@@ -269,9 +269,13 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   auto tile_q0 = [&](int t) { return (qt0 + t - (t / ntq) * ntq) * BQ; };
   auto issue = [&](int t, char* qt, char* ot) {
     const int i = t / ntq, q0 = tile_q0(t);
-    const long qi = sl.lse_base + (long)i * p.Sq + min(q0 + lane, nq - 1);
-    lraw = p.lse[qi];
-    draw = p.delta[qi];
+    // Only wave 0 publishes the statistics, so only it loads them: any load issued behind
+    // the copies waits in the same queue.
+    if (wave == 0) {
+      const long qi = sl.lse_base + (long)i * p.Sq + min(q0 + lane, nq - 1);
+      lraw = p.lse[qi];
+      draw = p.delta[qi];
+    }
     // Only waves 0..3 copy: right after the barrier the copies queue up in the memory
     // pipeline and stall the waves that issue them (32 KB at ~64 B/clock), and meanwhile
     // the other wave of each SIMD has its matrix unit to itself.
@@ -366,7 +370,13 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
       f32x16 dp0, dp1;
       scores_dp(vt, co, cd, dp0, dp1);
       compute(cq, co, cl, q0, 0, dp0);
+      // The two waves of a SIMD do the same work, but waves 0..3 start late (copy issue)
+      // and then win every tie (older waves issue first), so they finish early and wait at
+      // the barrier while their partner runs alone.  Waves 4..7 take priority for their
+      // second half, so both finish about together.
+      if (wave >= 4) __builtin_amdgcn_s_setprio(1);
       compute(cq, co, cl, q0, 1, dp1);
+      if (wave >= 4) __builtin_amdgcn_s_setprio(0);
     }
     if (more) publish_stats(j + 1, nl, nd);
     wait_tile_loads();
@@ -572,10 +582,14 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       keep_branch();
       mask_scores(vw, k0, 1, st1);
     }
+    // Waves 4..7 take priority from here to the step's end (see dkdv_block: waves 0..3
+    // start late and win ties).  Split workgroups, where every wave copies, keep equal ones.
+    if (!split && wave >= 4) __builtin_amdgcn_s_setprio(1);
     grad(kt, 0, ds0);
     weights(st1, dpt1, ds1);
     __builtin_amdgcn_sched_barrier(0);
     grad(kt, 1, ds1);
+    if (!split && wave >= 4) __builtin_amdgcn_s_setprio(0);
   };
 
   // Causal: keys past the workgroup's last query row are never seen.
