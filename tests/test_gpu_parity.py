@@ -218,6 +218,21 @@ def test_scale_argument(A):
     check_all(gpu_dense(A, t, scale=0.3), oracle_dense(t, scale=0.3), t)
 
 
+def test_wide_rows_many_heads(A):
+    """2048 heads of D = 128: rows of 512 KiB, so a 256-row tile copy spans 128 MiB of one
+    tensor (the buffer-resource ranges stay below 2^31 bytes up to H * D = 2^22, the
+    library's limit).  Sampled heads, first, middle and last, against the oracle."""
+    B, S, H, D = 1, 300, 2048, 128
+    t = I.small_case(B, S, S, H, D, seed=660)
+    g = gpu_dense(A, t)
+    for h in (0, 1029, H - 1):
+        sub = I.Tensors(*(x[:, :, h:h + 1] for x in (t.q, t.k, t.v, t.do)), None, None)
+        r = oracle_dense(sub)
+        for n in ("out", "dq", "dk", "dv"):
+            assert_parity(f"{n}[h{h}]", to_f64(g[n][:, :, h:h + 1]), r[n])
+        assert_lse(to_f64(g["lse"][:, h:h + 1]), r["lse"])
+
+
 def test_no_keys_and_fully_masked_rows(A):
     import torch
     # Sk = 0: every row has nothing to attend to
