@@ -372,6 +372,25 @@ def test_wan_shard_sampled(A):
         _invariants(gh, do)
 
 
+def test_long_sequence_sampled(A):
+    """One head of 65573 tokens (D = 64): 257 query tiles and 1025 key tiles per loop, a
+    ragged tail in both, row and key indices past 2^16.  Sampled rows (out, LSE, dQ) vs the
+    oracle, row by row; dK/dV, whose columns would need the oracle's full forward, by the
+    invariants that hold at any size."""
+    B, S, H, D = 1, 65573, 1, 64
+    t = I.small_case(B, S, S, H, D, seed=670)
+    g = gpu_dense(A, t)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 255, 256, S - 37, S - 1], rng.integers(0, S, 16)]))
+    q, k, v, do = (f64(x) for x in (t.q, t.k, t.v, t.do))
+    o_r, l_r = oracle.attn_fwd(q[:, rows], k, v)
+    assert_parity("out[long]", to_f64(g["out"][:, rows]), o_r)
+    assert_lse(to_f64(g["lse"][:, :, rows]), l_r)
+    _, dq_r, _, _ = oracle.attn_bwd(q[:, rows], k, v, o_r, l_r, do[:, rows], want_dkdv=False)
+    assert_parity("dq[long]", to_f64(g["dq"][:, rows]), dq_r)
+    _invariants({n: to_f64(g[n]) for n in ("dk", "dv")}, do)
+
+
 def test_varlen4_sampled(A):
     """Packed lengths (4096, 7000, 1234, 15000), H=24 D=128: two heads, sampled rows and
     columns of every sequence vs per-sequence oracle calls."""
