@@ -58,13 +58,17 @@ def lib():
     L.attn_bwd_ex.argtypes = [i, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_varlen_fwd_ex.argtypes = [i, vp, vp, i, i, f, i, vp, vp, vp, vp, vp, vp]
     L.attn_varlen_bwd_ex.argtypes = [i, vp, vp, i, i, f, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_varlen_fwd_gqa.argtypes = [i, vp, vp, i, i, i, f, i, vp, vp, vp, vp, vp, vp]
+    L.attn_varlen_bwd_gqa.argtypes = [i, vp, vp, i, i, i, f, i, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp]
     L.attn_bwd_gqa.argtypes = [i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_bwd_accum.argtypes = [i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.attn_cast_bf16.argtypes = [ctypes.c_int64, vp, vp, vp]
     for name in ("attn_abi_version", "attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                  "attn_varlen_fwd", "attn_varlen_bwd", "attn_lse_merge", "attn_bwd_accum",
                  "attn_cast_bf16", "attn_fwd_gqa", "attn_bwd_gqa", "attn_fwd_ex", "attn_bwd_ex",
-                 "attn_varlen_fwd_ex", "attn_varlen_bwd_ex"):
+                 "attn_varlen_fwd_ex", "attn_varlen_bwd_ex", "attn_varlen_fwd_gqa",
+                 "attn_varlen_bwd_gqa"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -242,12 +246,15 @@ def _thd(x, name):
 
 
 def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None, causal=False):
-    """Packed varlen forward: q/k/v (T,H,D) bf16, cu_seqlens int32[nseq+1] -> out (T,H,D), lse (H,T)."""
+    """Packed varlen forward: q (T,H,D), k/v (T,Hk,D) bf16 (Hk dividing H: grouped-query
+    heads), cu_seqlens int32[nseq+1] -> out (T,H,D), lse (H,T)."""
     torch = _torch()
     q3, k3, v3 = _thd(q, "q"), _thd(k, "k"), _thd(v, "v")
     T, H, D = q3.shape
-    for t, n in ((q3, "q"), (k3, "k"), (v3, "v")):
-        _want(t, n, (T, H, D), torch.bfloat16)
+    Hk = _kv_heads(q3[None], k3[None])
+    _want(q3, "q", (T, H, D), torch.bfloat16)
+    for t, n in ((k3, "k"), (v3, "v")):
+        _want(t, n, (T, Hk, D), torch.bfloat16)
     host, dev = _cu_args(cu_seqlens, q.device)
     nseq = host.numel() - 1
     if nseq < 0 or int(host[-1]) != T:
@@ -257,21 +264,25 @@ def attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None, causal=
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _want(_thd(out, "out"), "out", (T, H, D), torch.bfloat16)
     _want(lse, "lse", (H, T), torch.float32)
-    _check("attn_varlen_fwd", lib().attn_varlen_fwd_ex(nseq, _ptr(host), _ptr(dev), H, D, scale,
-                                                       CAUSAL if causal else 0, _ptr(q3),
-                                                       _ptr(k3), _ptr(v3), _ptr(out), _ptr(lse),
-                                                       _stream()))
+    _check("attn_varlen_fwd", lib().attn_varlen_fwd_gqa(nseq, _ptr(host), _ptr(dev), H, Hk, D,
+                                                        scale, CAUSAL if causal else 0, _ptr(q3),
+                                                        _ptr(k3), _ptr(v3), _ptr(out), _ptr(lse),
+                                                        _stream()))
     return out, lse
 
 
 def attn_varlen_bwd(q, k, v, lse, delta, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None,
                     causal=False):
-    """Packed varlen backward -> dq, dk, dv (T,H,D).  delta = attn_bwd_preprocess(out, dout)[0]."""
+    """Packed varlen backward -> dq (T,H,D), dk, dv (T,Hk,D).  delta = attn_bwd_preprocess(out,
+    dout)[0]."""
     torch = _torch()
     q3, k3, v3, o3 = _thd(q, "q"), _thd(k, "k"), _thd(v, "v"), _thd(dout, "dout")
     T, H, D = q3.shape
-    for t, n in ((q3, "q"), (k3, "k"), (v3, "v"), (o3, "dout")):
+    Hk = _kv_heads(q3[None], k3[None])
+    for t, n in ((q3, "q"), (o3, "dout")):
         _want(t, n, (T, H, D), torch.bfloat16)
+    for t, n in ((k3, "k"), (v3, "v")):
+        _want(t, n, (T, Hk, D), torch.bfloat16)
     if delta.dim() == 3:
         delta = delta[0]
     _want(lse, "lse", (H, T), torch.float32)
@@ -284,13 +295,14 @@ def attn_varlen_bwd(q, k, v, lse, delta, dout, cu_seqlens, scale=None, dq=None, 
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _want(_thd(t, n), n, (T, H, D), torch.bfloat16)
-    _check("attn_varlen_bwd", lib().attn_varlen_bwd_ex(nseq, _ptr(host), _ptr(dev), H, D, scale,
-                                                       CAUSAL if causal else 0, _ptr(q3),
-                                                       _ptr(k3), _ptr(v3), _ptr(lse), _ptr(delta),
-                                                       _ptr(o3), _ptr(dq), _ptr(dk), _ptr(dv),
-                                                       _stream()))
+    _want(_thd(dq, "dq"), "dq", (T, H, D), torch.bfloat16)
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _want(_thd(t, n), n, (T, Hk, D), torch.bfloat16)
+    _check("attn_varlen_bwd", lib().attn_varlen_bwd_gqa(nseq, _ptr(host), _ptr(dev), H, Hk, D,
+                                                        scale, CAUSAL if causal else 0, _ptr(q3),
+                                                        _ptr(k3), _ptr(v3), _ptr(lse), _ptr(delta),
+                                                        _ptr(o3), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                        _stream()))
     return dq, dk, dv
 
 

@@ -17,7 +17,7 @@ using attn::FwdParams;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
 // The backward starts its score accumulators from -LSE/scale; the lower bound keeps that
@@ -343,13 +343,21 @@ int attn_varlen_fwd(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_
 int attn_varlen_fwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
                        int H, int D, float scale, int flags, const void* q, const void* k,
                        const void* v, void* out, float* lse, void* stream) {
+  return attn_varlen_fwd_gqa(nseq, cu_seqlens_host, cu_seqlens_dev, H, H, D, scale, flags, q, k,
+                             v, out, lse, stream);
+}
+
+int attn_varlen_fwd_gqa(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                        int H, int Hk, int D, float scale, int flags, const void* q,
+                        const void* k, const void* v, void* out, float* lse, void* stream) {
   if (!cu_seqlens_host || !cu_seqlens_dev) return ATTN_ERR_NULL;
   if (flags & ~ATTN_CAUSAL) return ATTN_ERR_SHAPE;
   int T = 0, maxlen = 0;
-  const int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
+  int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
+  if (st == ATTN_OK) st = check_kv_heads(H, Hk);
   if (st != ATTN_OK) return st;
-  const bool ht = (long)T * H > 0;
-  if (missing(q, ht) || missing(k, ht) || missing(v, ht) || missing(out, ht) || missing(lse, ht))
+  const bool ht = (long)T * H > 0, hk = (long)T * Hk > 0;
+  if (missing(q, ht) || missing(k, hk) || missing(v, hk) || missing(out, ht) || missing(lse, ht))
     return ATTN_ERR_NULL;
   if ((long)T * H == 0) return ATTN_OK;
   FwdParams p{};
@@ -363,8 +371,8 @@ int attn_varlen_fwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
   p.B = nseq;
   p.Sq = p.Sk = T;
   p.H = H;
-  p.Hk = H;
-  p.G = 1;
+  p.Hk = Hk;
+  p.G = H / Hk;
   p.causal = flags & ATTN_CAUSAL;
   p.n_qtiles = (int)cdiv(maxlen, attn::kFwdBlockM);
   p.order = seq_order(nseq, cu_seqlens_host);
@@ -385,19 +393,28 @@ int attn_varlen_bwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
                        int H, int D, float scale, int flags, const void* q, const void* k,
                        const void* v, const float* lse, const float* delta, const void* dout,
                        void* dq, void* dk, void* dv, void* stream) {
+  return attn_varlen_bwd_gqa(nseq, cu_seqlens_host, cu_seqlens_dev, H, H, D, scale, flags, q, k,
+                             v, lse, delta, dout, dq, dk, dv, stream);
+}
+
+int attn_varlen_bwd_gqa(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                        int H, int Hk, int D, float scale, int flags, const void* q,
+                        const void* k, const void* v, const float* lse, const float* delta,
+                        const void* dout, void* dq, void* dk, void* dv, void* stream) {
   if (!cu_seqlens_host || !cu_seqlens_dev) return ATTN_ERR_NULL;
   if (flags & ~ATTN_CAUSAL) return ATTN_ERR_SHAPE;
   int T = 0, maxlen = 0;
-  const int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
+  int st = check_varlen(nseq, cu_seqlens_host, H, D, scale, &T, &maxlen);
+  if (st == ATTN_OK) st = check_kv_heads(H, Hk);
   if (st != ATTN_OK) return st;
-  const bool ht = (long)T * H > 0;
-  if (missing(q, ht) || missing(k, ht) || missing(v, ht) || missing(lse, ht) ||
-      missing(delta, ht) || missing(dout, ht) || missing(dq, ht) || missing(dk, ht) ||
-      missing(dv, ht))
+  const bool ht = (long)T * H > 0, hk = (long)T * Hk > 0;
+  if (missing(q, ht) || missing(k, hk) || missing(v, hk) || missing(lse, ht) ||
+      missing(delta, ht) || missing(dout, ht) || missing(dq, ht) || missing(dk, hk) ||
+      missing(dv, hk))
     return ATTN_ERR_NULL;
   if ((long)T * H == 0) return ATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  BwdParams p = bwd_params(nseq, T, T, H, H, scale, q, k, v, nullptr, lse, delta, dout, dq, dk,
+  BwdParams p = bwd_params(nseq, T, T, H, Hk, scale, q, k, v, nullptr, lse, delta, dout, dq, dk,
                            dv, cu_seqlens_dev);
   p.causal = flags & ATTN_CAUSAL;
   p.order = seq_order(nseq, cu_seqlens_host);

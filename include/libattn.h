@@ -195,6 +195,19 @@ int attn_varlen_bwd_ex(int nseq, const int32_t* cu_seqlens_host, const int32_t* 
                        const void* v, const float* lse, const float* delta, const void* dout,
                        void* dq, void* dk, void* dv, void* stream);
 
+/* Varlen with grouped-query heads (as attn_fwd_gqa / attn_bwd_gqa, inside each sequence):
+ * q, out, dout, dq are (T, H, D), k, v, dk, dv (T, Hk, D), lse and delta (H, T); query head
+ * h reads key/value head h / (H / Hk), and dk, dv of a key/value head sum its H / Hk query
+ * heads.  Hk must divide H (else ATTN_ERR_SHAPE); flags as attn_varlen_fwd_ex.  The
+ * attn_varlen_*_ex calls are these with Hk = H. */
+int attn_varlen_fwd_gqa(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                        int H, int Hk, int D, float scale, int flags, const void* q,
+                        const void* k, const void* v, void* out, float* lse, void* stream);
+int attn_varlen_bwd_gqa(int nseq, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                        int H, int Hk, int D, float scale, int flags, const void* q,
+                        const void* k, const void* v, const float* lse, const float* delta,
+                        const void* dout, void* dq, void* dk, void* dv, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

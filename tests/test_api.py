@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
             "attn_varlen_bwd_ex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 4
+    assert L.attn_abi_version() == 5
     assert L.attn_status_str(0) == b"ok"
     assert L.attn_status_str(4) == b"invalid cu_seqlens"
 
@@ -184,6 +184,14 @@ def test_varlen_validation(L):
     assert call([0]) == (OK, OK)                # no sequences: nothing to do
     assert call([0, 0, 0]) == (OK, OK)          # empty sequences: T = 0
     assert call([0, 5, 9], H=0) == (OK, OK)
+    # grouped-query heads: Hk must divide H
+    arr, p = _cu([0, 5, 9])
+    for Hk, want in ((3, SHAPE), (0, SHAPE), (-1, SHAPE)):
+        assert L.attn_varlen_fwd_gqa(2, p, P, 4, Hk, 128, 0.1, 0, P, P, P, P, P, None) == want
+        assert L.attn_varlen_bwd_gqa(2, p, P, 4, Hk, 128, 0.1, 0, P, P, P, P, P, P, P, P, P,
+                                     None) == want
+    assert L.attn_varlen_fwd_gqa(2, p, P, 4, 2, 128, 0.1, 2, P, P, P, P, P, None) == SHAPE
+    assert L.attn_varlen_fwd_gqa(2, p, P, 4, 2, 128, 0.1, 0, P, None, P, P, P, None) == NULL
     arr, p = _cu([0, 4])
     assert L.attn_varlen_fwd(1, None, P, 2, 64, 0.1, P, P, P, P, P, None) == NULL
     assert L.attn_varlen_fwd(1, p, None, 2, 64, 0.1, P, P, P, P, P, None) == NULL
