@@ -221,7 +221,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
   // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
   // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt before every use from the
-  // step-0 offsets, which keeps 14 registers free for the loop.
+  // step-0 offsets (3 registers instead of 16 held through the loop).
   int qoff0 = tile_off<D>(l32, hl), tr0[2];
   {
     int t[NMB][2];
@@ -480,9 +480,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
   // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
   // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt at every step from the step-0
-  // offsets, which keeps 14 registers free for the loop.  The offsets also carry the wave
-  // group's distance to its own tiles (GB, a multiple of 256 bytes, which the XORs leave
-  // alone), so the tile addresses stay constants.
+  // offsets (3 registers instead of 16 held through the loop).  The offsets also carry the
+  // wave group's distance to its own tiles (GB, a multiple of 256 bytes, which the XORs
+  // leave alone), so the tile addresses stay constants.
   int koff0 = tile_off<D>(l32, hl) + grp * GB, tr0[2];
   {
     int troff[NMB][2];
