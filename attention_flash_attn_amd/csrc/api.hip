@@ -1,12 +1,14 @@
 // api.hip -- the C ABI of libattn: argument validation on the host, then launches.
 //
 // Every check runs before anything is enqueued, so a call that returns an
-// error has launched nothing and written nothing.  No allocation, no state,
-// no synchronisation: the caller's stream orders the work.
+// error has launched nothing and written nothing.  No allocation, no
+// synchronisation (the caller's stream orders the work), and no state beyond a
+// per-device cache of the compute-unit count that sizes the grids.
 #include <math.h>
 #include <limits.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "libattn.h"
 #include "common.hpp"
@@ -106,19 +108,21 @@ const char* attn_status_str(int status) {
 
 int attn_abi_version(void) { return kAbiVersion; }
 
-// Compute units of the device that runs `stream` (cached per device).
+// Compute units of the device that runs `stream`.  The count is a fixed property of the
+// device, so it is cached per device: the library's only state.  Concurrent first calls
+// may both query it and store the same value; the atomics make that race well defined.
 static int cu_count(hipStream_t stream) {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipStreamGetDevice(stream, &dev) != hipSuccess) dev = 0;
   if (dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Grid of the forward launch: one block per whole query tile, except that when the last
@@ -165,7 +169,7 @@ int attn_fwd_ex(int B, int Sq, int Sk, int H, int Hk, int D, float scale, int fl
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);
   p.v = static_cast<const __bf16*>(v);
-  p.mask = key_mask;
+  p.mask = Sk > 0 ? key_mask : nullptr;  // with no keys there is no mask byte to read
   p.out = static_cast<__bf16*>(out);
   p.lse = lse;
   p.cu = nullptr;
@@ -206,7 +210,7 @@ static BwdParams bwd_params(int B, int Sq, int Sk, int H, int Hk, float scale, c
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);
   p.v = static_cast<const __bf16*>(v);
-  p.mask = key_mask;
+  p.mask = Sk > 0 ? key_mask : nullptr;  // with no keys there is no mask byte to read
   p.lse = lse;
   p.delta = delta;
   p.dout = static_cast<const __bf16*>(dout);

@@ -345,8 +345,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     l_run = a * l_run + b * lb;
     m_run = m;
   } else {
-  mbytes = kv.load(0);
   if (ntiles > 0) {
+    mbytes = kv.load(0);
     if (grp_b) {
       kld.issue(sK0, kbase, rsk, 0, nk, krow);
       wait_tile_loads();

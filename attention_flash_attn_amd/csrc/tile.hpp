@@ -127,7 +127,8 @@ struct KeyValidity {
   int nk;
   __device__ __forceinline__ uint32_t load(int k0) const {
     uint32_t b = 1u;
-    if (mask) b = mask[min(k0 + (int)(threadIdx.x & 63), nk - 1)];
+    // nk = 0: no byte of the mask exists (the clamped index would be -1)
+    if (mask && nk > 0) b = mask[min(k0 + (int)(threadIdx.x & 63), nk - 1)];
     return b;
   }
   __device__ __forceinline__ uint64_t word(int k0, uint32_t b) const {

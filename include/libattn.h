@@ -31,12 +31,18 @@
  *    It is broadcast over heads and queries, i.e. a (B,1,1,Sk) mask.  A
  *    per-head (B,H,1,Sk) mask is not expressible and must be rejected by the
  *    caller before any work (diffusers PR #14834, "Unsupported cases").
- *  - Supported: head dim D in {64, 128}; Hk == H (no GQA); Sq may differ from Sk.
+ *  - Supported: head dim D in {64, 128}; Sq may differ from Sk.  The plain calls
+ *    take Hk == H key/value heads; the _gqa and _ex calls take any Hk that
+ *    divides H (grouped-query attention, below).
+ *  - key_mask is read only for keys that exist: with Sk = 0 it is never read.
  *  - A query row whose keys are all masked gets out = 0, LSE = -inf, dQ = 0.
  *  - A tensor pointer may be NULL only when that tensor has no elements (e.g. k
  *    and v when Sk = 0); otherwise NULL is ATTN_ERR_NULL.
  *  - Every tensor pointer is device memory the caller allocated and owns; the
- *    library allocates nothing, keeps no state and is reentrant.  Calls only
+ *    library allocates nothing and is reentrant.  Its only state is a per-device
+ *    cache of the compute-unit count (read once per device, with atomics, to size
+ *    the grids); results therefore depend on the device a call runs on (see
+ *    attn_fwd / attn_bwd on reproducibility).  Calls only
  *    enqueue work on `stream` (a hipStream_t; NULL = the default stream) and
  *    never synchronise.  Inputs must not alias outputs.
  *  - Every argument is checked on the host before any launch.  A call that
@@ -72,7 +78,11 @@ int attn_abi_version(void);
  * Forward: q (B,Sq,H,D), k and v (B,Sk,H,D) bf16 -> out (B,Sq,H,D) bf16 and
  * lse (B,H,Sq) fp32.  scale multiplies q.k: finite and at least 2^-64 (callers
  * normally pass 1/sqrt(D)).
- * key_mask may be NULL.
+ * key_mask may be NULL.  Results are bitwise reproducible for a given shape on a
+ * given device: when the grid's last round of workgroups would leave most compute
+ * units idle, its query tiles run as split workgroups (chosen from the device's
+ * compute-unit count) whose two key halves are combined at the end, which rounds
+ * out and lse slightly differently from a whole tile.
  */
 int attn_fwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, void* out, float* lse, void* stream);
@@ -90,7 +100,10 @@ int attn_bwd_preprocess(int B, int S, int H, int D, const void* out, const void*
  * write dq (B,Sq,H,D), dk and dv (B,Sk,H,D), all bf16.  Keys excluded by
  * key_mask get dk = dv = 0 exactly.  dK/dV and dQ are produced by separate
  * workgroups (of one launch), each owning its output rows, so no atomics are
- * used and results are bitwise reproducible.  key_mask may be NULL.
+ * used and results are bitwise reproducible for a given shape on a given device
+ * (the last dQ tiles of a dense call may run as split workgroups, chosen from the
+ * device's compute-unit count, which sum their two key halves separately; another
+ * device can therefore round dQ differently).  key_mask may be NULL.
  */
 int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, const void* k,
              const void* v, const uint8_t* key_mask, const float* lse, const float* delta,
@@ -102,8 +115,9 @@ int attn_bwd(int B, int Sq, int Sk, int H, int D, float scale, const void* q, co
  * quoted in diffusers PR #14341, reporter's tables, state): as attn_fwd / attn_bwd, but k
  * and v (and dk, dv) are (B,Sk,Hk,D) with H = G * Hk, and query head h attends with key /
  * value head h / G.  dk, dv of a key/value head sum the contributions of its G query heads
- * (computed in one workgroup per key tile, no atomics, bitwise reproducible).  Hk that does
- * not divide H: ATTN_ERR_SHAPE.  attn_fwd / attn_bwd are these calls with Hk = H.
+ * (computed in one workgroup per key tile, no atomics, bitwise reproducible for a given
+ * shape and device).  Hk that does not divide H: ATTN_ERR_SHAPE.  attn_fwd / attn_bwd are
+ * these calls with Hk = H.
  */
 int attn_fwd_gqa(int B, int Sq, int Sk, int H, int Hk, int D, float scale, const void* q,
                  const void* k, const void* v, const uint8_t* key_mask, void* out, float* lse,

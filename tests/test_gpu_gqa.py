@@ -110,18 +110,6 @@ def test_gqa_s8192_sampled(A):
     _sampled(A, t, H, Hk, rows, cols, kv_head=1)
 
 
-def test_wan_shard_gqa_sampled(A):
-    """The Wan shard's 10 query heads over 2 key/value heads (the bench's GQA workload):
-    sampled rows and key columns of key/value head 1 (query heads 5..9)."""
-    w = I.WORKLOADS["wan_shard_gqa"]
-    t = I.draw_workload(w)
-    S = w.S
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 16)]))
-    cols = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 16)]))
-    _sampled(A, t, w.H, w.Hk, rows, cols, kv_head=1)
-
-
 @pytest.mark.parametrize("D,causal", [(64, False), (128, False), (128, True)],
                          ids=["D64", "D128", "D128_causal"])
 def test_varlen_gqa(A, D, causal):

@@ -245,6 +245,39 @@ def test_no_keys_and_fully_masked_rows(A):
     check_all(gpu_dense(A, t), oracle_dense(t), t)
 
 
+def test_no_keys_with_mask_pointer_c_abi(A):
+    """Sk = 0 with a non-null key_mask, straight through the C ABI (the binding passes NULL
+    for an empty mask): no mask byte exists, so none may be read, and every row has nothing
+    to attend to (out = 0, LSE = -inf, dQ = 0).  The mask pointer sits in the middle of a
+    larger allocation, so the call stays in bounds whatever the kernels read."""
+    import ctypes
+    import torch
+    L = A.lib()
+    B, Sq, H, D = 2, 300, 3, 128
+    q = torch.randn(B, Sq, H, D, device="cuda").to(torch.bfloat16)
+    do = torch.randn_like(q)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, Sq), float("nan"), device="cuda")
+    arena = torch.ones(1 << 16, dtype=torch.uint8, device="cuda")
+    mask = ctypes.c_void_p(arena.data_ptr() + (1 << 15))
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    scale = 1.0 / np.sqrt(D)
+    for Hk, flags in ((H, 0), (1, 0), (H, 1)):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        assert L.attn_fwd_ex(B, Sq, 0, H, Hk, D, scale, flags, vp(q), None, None, mask, vp(out),
+                             vp(lse), stream) == 0
+        delta = torch.full((B, H, Sq), float("nan"), device="cuda")
+        assert L.attn_bwd_preprocess(B, Sq, H, D, vp(out), vp(do), vp(delta), stream) == 0
+        dq = torch.full_like(q, float("nan"))
+        assert L.attn_bwd_ex(B, Sq, 0, H, Hk, D, scale, flags, vp(q), None, None, mask, vp(lse),
+                             vp(delta), vp(do), vp(dq), None, None, stream) == 0
+        torch.cuda.synchronize()
+        assert torch.all(out == 0) and torch.all(torch.isneginf(lse)), (Hk, flags)
+        assert torch.all(delta == 0) and torch.all(dq == 0), (Hk, flags)
+
+
 def test_deterministic_and_mask_equivalence(A):
     import torch
     t = I.small_case(2, 200, 200, 2, 128, seed=9)
@@ -320,20 +353,6 @@ def test_mask_s4096_sampled_heads(A):
             assert np.all(to_f64(g["dk"][0, 3001:]) == 0) and np.all(to_f64(g["dv"][0, 3001:]) == 0)
 
 
-def _sampled_head_check(g, q, k, v, do, rows, cols, tag):
-    """q/k/v/do: fp64 (1, S, 1, D) of one head; g: that head's GPU outputs (fp64)."""
-    o_r, l_r = oracle.attn_fwd(q[:, rows], k, v)
-    assert_parity(f"out{tag}", g["out"][:, rows], o_r)
-    assert_lse(g["lse"][:, :, rows], l_r)
-    _, dq_r, _, _ = oracle.attn_bwd(q[:, rows], k, v, o_r, l_r, do[:, rows], want_dkdv=False)
-    assert_parity(f"dq{tag}", g["dq"][:, rows], dq_r)
-    out_full, lse_full = oracle.attn_fwd(q, k, v)  # every row's LSE and out feed dK/dV
-    _, _, dk_r, dv_r = oracle.attn_bwd(q, k[:, cols], v[:, cols], out_full, lse_full, do,
-                                       want_dq=False)
-    assert_parity(f"dk{tag}", g["dk"][:, cols], dk_r)
-    assert_parity(f"dv{tag}", g["dv"][:, cols], dv_r)
-
-
 def _invariants(g, do):
     """Oracle-free properties of one head at any size: sum_j dK_j = 0 and
     sum_j dV_j = sum_i dO_i (softmax shift invariance / rows of P summing to one).
@@ -347,29 +366,6 @@ def _invariants(g, do):
     ref = do[0, :, 0].sum(0)
     tol_v = 8 * 2.0 ** -8 * np.sqrt(np.sum(dv ** 2, axis=0)) + 1e-3
     assert np.all(np.abs(dv.sum(0) - ref) <= tol_v), np.max(np.abs(dv.sum(0) - ref) / tol_v)
-
-
-def test_wan_shard_sampled(A):
-    """B=1 N=27280 H=10 D=128 (one Ulysses rank of the Wan layer): sampled rows/columns of
-    two heads vs the oracle, plus invariants on every head."""
-    w = I.WORKLOADS["wan_shard"]
-    t = I.draw_workload(w)
-    g = gpu_dense(A, t)
-    rng = np.random.default_rng(0)
-    S = w.S
-    rows = np.unique(np.concatenate([[0, 1, S - 16, S - 1], rng.integers(0, S, 28)]))
-    cols = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 30)]))
-    # head 9, rows 15616.. : the forward's split workgroups (the last 46 of 1070 query tiles)
-    rows9 = np.unique(np.concatenate([[15616, 15743, 15744, 27279], rng.integers(15616, S, 12)]))
-    for h, rws in ((0, rows), (7, rows), (9, rows9)):
-        q, k, v, do = (f64(x[:, :, h:h + 1]) for x in (t.q, t.k, t.v, t.do))
-        gh = {n: to_f64(g[n][:, :, h:h + 1]) for n in ("out", "dq", "dk", "dv")}
-        gh["lse"] = to_f64(g["lse"][:, h:h + 1])
-        _sampled_head_check(gh, q, k, v, do, rws, cols, f"[h{h}]")
-    for h in range(w.H):
-        do = f64(t.do[:, :, h:h + 1])
-        gh = {n: to_f64(g[n][:, :, h:h + 1]) for n in ("dk", "dv")}
-        _invariants(gh, do)
 
 
 def test_long_sequence_sampled(A):
@@ -389,24 +385,3 @@ def test_long_sequence_sampled(A):
     _, dq_r, _, _ = oracle.attn_bwd(q[:, rows], k, v, o_r, l_r, do[:, rows], want_dkdv=False)
     assert_parity("dq[long]", to_f64(g["dq"][:, rows]), dq_r)
     _invariants({n: to_f64(g[n]) for n in ("dk", "dv")}, do)
-
-
-def test_varlen4_sampled(A):
-    """Packed lengths (4096, 7000, 1234, 15000), H=24 D=128: two heads, sampled rows and
-    columns of every sequence vs per-sequence oracle calls."""
-    w = I.WORKLOADS["varlen4"]
-    t = I.draw_workload(w)
-    H, D = w.H, w.D
-    g = gpu_varlen(A, I.Tensors(t.q[0], t.k[0], t.v[0], t.do[0], None, t.cu_seqlens), H, D)
-    cu = t.cu_seqlens
-    rng = np.random.default_rng(1)
-    for h in (3, 20):
-        for n in range(len(cu) - 1):
-            a, b = int(cu[n]), int(cu[n + 1])
-            L = b - a
-            q, k, v, do = (f64(x[:, a:b, h:h + 1]) for x in (t.q, t.k, t.v, t.do))
-            gh = {nm: to_f64(g[nm][None, a:b, h:h + 1]) for nm in ("out", "dq", "dk", "dv")}
-            gh["lse"] = to_f64(g["lse"][h:h + 1, a:b])[None]
-            rows = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 10)]))
-            cols = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 10)]))
-            _sampled_head_check(gh, q, k, v, do, rows, cols, f"[h{h},seq{n}]")
