@@ -251,8 +251,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   {
     TileLoader<D, BN, NW> kvld;
     kvld.init(rsk, same_row);
-    kvld.issue(kstage, kbase, rsk, kb0, nk, same_row);
-    kvld.issue(sm.v, vbase, rsk, kb0, nk, same_row);
+    kvld.issue(kstage, kbase, rsk, kb0, nk);
+    kvld.issue(sm.v, vbase, rsk, kb0, nk);
   }
   TileLoader<D, BQ, 4> ld;  // used by waves 0..3
   ld.init(rs, qrow_of);
@@ -280,8 +280,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     // pipeline and stall the waves that issue them (32 KB at ~64 B/clock), and meanwhile
     // the other wave of each SIMD has its matrix unit to itself.
     if (wave < 4) {
-      ld.issue(qt, qbase + (long)i * D, rs, q0, nq, qrow_of);
-      ld.issue(ot, obase + (long)i * D, rs, q0, nq, qrow_of);
+      ld.issue(qt, qbase + (long)i * D, rs, q0, nq);
+      ld.issue(ot, obase + (long)i * D, rs, q0, nq);
     }
   };
   // Published per row: -LSE/scale and -delta, the starting values of the S and dP
@@ -511,8 +511,8 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   // SIMD, keep the matrix units busy.  In a split workgroup each group copies its own tiles.
   auto issue = [&](int k0, char* kt, char* vt) {
     if (split || wave < 4) {
-      ld.issue(kt + grp * GB, kbase, rsk, k0, nk, krow_of);
-      ld.issue(vt + grp * GB, vbase, rsk, k0, nk, krow_of);
+      ld.issue(kt + grp * GB, kbase, rsk, k0, nk);
+      ld.issue(vt + grp * GB, vbase, rsk, k0, nk);
     }
   };
 
@@ -520,6 +520,11 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
   const float c2 = p.c2;
+  // The dP^T accumulators start from the row's -delta (16 registers held through the loop,
+  // 32 subtractions a step fewer).
+  f32x16 ndl16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
 
   // Per 32-key half kb of a tile: scores A (S^T, dP^T MFMAs), weights B (VALU: P,
   // dS), gradient C (dQ^T MFMAs), issued as A0 | A1 B0 | C0 B1 | C1 with hard
@@ -527,7 +532,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   auto scores = [&](const char* kt, const char* vt, int kb, f32x16& st, f32x16& dpt) {
     const int rb = kb * 32 * RB;
     st = f32x16{};
-    dpt = f32x16{};
+    dpt = ndl16;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) st = mfma32(lds_row16(kt, rb + koff[ks]), qreg[ks], st);
 #pragma unroll
@@ -551,7 +556,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
-      dpt[r] = st[r] * (dpt[r] - dl);
+      dpt[r] = st[r] * dpt[r];
     }
     ds[0] = pack8(dpt, 0);
     ds[1] = pack8(dpt, 8);

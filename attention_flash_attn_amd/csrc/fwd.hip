@@ -216,16 +216,38 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
           sacc[kb][r] = on ? sacc[kb][r] : -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // Weights against the row's current reference m_run, with no max over the tile: the
+    // exponent arguments y = c2 s - m_run stay in sacc, and the tile is accepted unless some
+    // row's tile sum exceeds 2^14 (or overflows), which keeps every weight below 2^14.  The
+    // first tile of a row (no reference yet) and the rare rejected tile form the tile max
+    // from y, move the reference up by it, rescale O and l, and recompute the weights.
+    const bool first = __ballot(m_run == -INFINITY) != 0;
+    const float muse = m_run == -INFINITY ? 0.f : m_run;
+    float la = 0.f, lb = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = wave_max_halves(mx);
-    const float mt = mx * c2;
-    if (__ballot(mt > m_run + 8.0f)) {
+      for (int h = 0; h < 2; ++h) {
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float y = fmaf(sacc[kb][8 * h + r], c2, -muse);
+          sacc[kb][8 * h + r] = y;
+          x[r] = __builtin_amdgcn_exp2f(y);
+          if (r & 1) lb += x[r]; else la += x[r];
+        }
+        pk[kb][h] = pack8(x, 0);
+      }
+    float lt = la + lb;
+    if (first || __ballot(!(lt <= 0x1p14f))) {
       keep_branch();
-      const float mnew = fmaxf(m_run, mt);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = wave_max_halves(mx);
+      const float mnew = fmaxf(m_run, muse + mx);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
       l_run *= alpha;
 #pragma unroll
@@ -233,19 +255,23 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
       m_run = mnew;
-    }
-    const float muse = m_run == -INFINITY ? 0.f : m_run;
+      const float d = mnew == -INFINITY ? 0.f : mnew - muse;
+      la = lb = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -muse));
-        sacc[kb][r] = x;
-        l_run += x;
-      }
-      pk[kb][0] = pack8(sacc[kb], 0);
-      pk[kb][1] = pack8(sacc[kb], 8);
+        for (int h = 0; h < 2; ++h) {
+          f32x16 x;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            x[r] = __builtin_amdgcn_exp2f(sacc[kb][8 * h + r] - d);
+            if (r & 1) lb += x[r]; else la += x[r];
+          }
+          pk[kb][h] = pack8(x, 0);
+        }
+      lt = la + lb;
     }
+    l_run += lt;
   };
   // MFMA phase of tile j: O += P(j-1) V(j-1), then S(j).  Group B then waits for the
   // copies it issued in its previous phase.
@@ -262,8 +288,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   auto softmax_phase = [&](int j, char* __restrict__ kn, char* __restrict__ vn)
       __attribute__((always_inline)) {
     if (grp_b) {
-      if (j + 2 < ntiles) kld.issue(kn, kbase, rsk, (j + 2) * BN, nk, krow);
-      if (j + 1 < ntiles) vld.issue(vn, vbase, rsk, (j + 1) * BN, nk, vrow);
+      if (j + 2 < ntiles) kld.issue(kn, kbase, rsk, (j + 2) * BN, nk);
+      if (j + 1 < ntiles) vld.issue(vn, vbase, rsk, (j + 1) * BN, nk);
     }
     if (vw_s != 0) softmax(j * BN, vw_s);
   };
@@ -297,8 +323,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if (more) {
         vw_next = tile_word(j + 1, mbytes);
         mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
-        gk.issue(kn, kbase, rsk, (j + 1) * BN, nk, krow);
-        gv.issue(vn, vbase, rsk, (j + 1) * BN, nk, vrow);
+        gk.issue(kn, kbase, rsk, (j + 1) * BN, nk);
+        gv.issue(vn, vbase, rsk, (j + 1) * BN, nk);
       }
       if (j < t1 && vw != 0) {
         gemm_s(kt);
@@ -312,8 +338,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     if (t0 < t1) {
       vw = tile_word(t0, kv.load(t0 * BN));
       mbytes = kv.load((t0 + 1) * BN);
-      gk.issue(gb, kbase, rsk, t0 * BN, nk, krow);
-      gv.issue(gb + 2 * TILE, vbase, rsk, t0 * BN, nk, vrow);
+      gk.issue(gb, kbase, rsk, t0 * BN, nk);
+      gv.issue(gb + 2 * TILE, vbase, rsk, t0 * BN, nk);
     }
     wait_tile_loads();
     __syncthreads();
@@ -348,13 +374,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   if (ntiles > 0) {
     mbytes = kv.load(0);
     if (grp_b) {
-      kld.issue(sK0, kbase, rsk, 0, nk, krow);
+      kld.issue(sK0, kbase, rsk, 0, nk);
       wait_tile_loads();
     }
     __syncthreads();
     if (grp_b) {  // phase 0 (group A: MFMAs of tile 0)
-      if (1 < ntiles) kld.issue(sK1, kbase, rsk, BN, nk, krow);
-      vld.issue(sV0, vbase, rsk, 0, nk, vrow);
+      if (1 < ntiles) kld.issue(sK1, kbase, rsk, BN, nk);
+      vld.issue(sV0, vbase, rsk, 0, nk);
       __syncthreads();
     }
     // even j: K(j) in sK0, V(j) in sV0; odd j: sK1, sV1

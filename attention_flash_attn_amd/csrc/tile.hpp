@@ -59,9 +59,10 @@ __device__ __forceinline__ bf16x8 lds_tr8(const char* tile, int off_lo, int off_
 // keeps only 32-bit offsets.  Lane-dependent parts of the offsets are fixed per kernel,
 // so they are computed once: off[i] is the byte offset, from the tile's first row, of the
 // 16-byte chunk this lane fetches with its i-th instruction.  row_of(r) maps tile row r
-// to its row offset within the tile (a permutation of 0..ROWS-1).  A tile that runs past
-// the last valid row re-reads that row instead (a tail tile only), so every access stays
-// inside the tensor.
+// to its row offset within the tile (a permutation of 0..ROWS-1).  In a tile that runs
+// past the last valid row, the copies of the missing rows fall outside the buffer range
+// and fill their LDS with zeros (issue() below): every access stays inside the tensor, and
+// a tail tile costs no per-lane work.
 template <int D, int ROWS, int NW>
 struct TileLoader {
   static constexpr int CPR = D / 8;            // chunks per row
@@ -84,35 +85,21 @@ struct TileLoader {
     }
   }
 
-  // Buffer resource whose byte 0 is row row0 of the tensor whose row 0 (this head) is at
-  // `base`, covering the ROWS rows of a tile (the callers keep ROWS * 2 * rs < 2^32).
-  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16* base, long rs, int row0) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (long)row0 * rs), (short)0,
-                                             (int)(ROWS * 2 * rs), kBufferFlags);
-  }
-
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char* tile, int i, uint32_t o) const {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (wv + i * NW) * 1024), 16, o, 0, 0, 0);
   }
 
-  // Copy rows [row0, row0 + ROWS) of the tensor whose row 0 (this head) is at `base`;
-  // only rows < nrows exist.
-  template <typename RowOf>
-  __device__ __forceinline__ void issue(char* tile, const bf16* base, long rs, int row0, int nrows,
-                                        RowOf row_of) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc(base, rs, row0);
-    if (row0 + ROWS <= nrows) {
+  // Copy rows [row0, row0 + ROWS) of the tensor whose row 0 (this head) is at `base`; only
+  // rows < nrows exist.  The buffer resource starts at row row0 and its byte range ends at
+  // the last of them (min(ROWS, nrows - row0) rows of 2 rs bytes; the callers keep
+  // ROWS * 2 * rs < 2^31), so the lanes of rows past the end read nothing and the hardware
+  // writes zeros to their 16 bytes of LDS.
+  __device__ __forceinline__ void issue(char* tile, const bf16* base, long rs, int row0, int nrows) const {
+    const int n = min(ROWS, nrows - row0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(base + (long)row0 * rs), (short)0, (int)(n * 2 * rs), kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) load(r, tile, i, off[i]);
-    } else {
-      const int lane = threadIdx.x & 63, last = nrows - 1 - row0;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int rr = (wv + i * NW) * RPI + lane / CPR;
-        const int want = row_of(rr), have = min(want, last);
-        load(r, tile, i, (uint32_t)((long)off[i] + 2 * (long)(have - want) * rs));
-      }
-    }
+    for (int i = 0; i < NI; ++i) load(r, tile, i, off[i]);
   }
 };
 

@@ -19,12 +19,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "attention_flash_attn_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Spill bytes per lane allowed per kernel instance (demangled name).  The dense D = 128
-# backward stores one register (4 B, padded to 8) before its dK/dV query loop and reloads it
-# after the loop; every other kernel must not spill at all.
+# Spill bytes per lane allowed per kernel instance (demangled name).  The D = 128 backward
+# holds 16 registers of the row's -delta through its dQ key loop; the dense instance then
+# stores three registers before that loop and reloads them after it, the varlen instance
+# (sequence bounds, longest-first order) six, one of them reloaded in the loop.  Every
+# other kernel must not spill at all.
 MAX_SCRATCH = {
-    "attn::bwd_kernel<128, false, false>": 8,
-    "attn::bwd_kernel<128, false, true>": 8,
+    "attn::bwd_kernel<128, false, false>": 16,
+    "attn::bwd_kernel<128, true, false>": 24,
 }
 
 
