@@ -125,20 +125,35 @@ static int cu_count(hipStream_t stream) {
   return n;
 }
 
-// Grid of the forward launch: one block per whole query tile, except that when the last
-// round of blocks would fill at most half of the CUs, those last `rem` tiles run as 2 rem
-// split blocks (half the rows, the keys shared out between the two wave groups), which
-// take about half as long.  Only where the tiles are of equal length (`may_split`: dense,
-// non-causal).
+// Grid of the forward launch: one block per whole query tile, except that the last
+// partial round of `rem` tiles of a grid of at least one full round may run as S split
+// blocks per tile (S = 2 or 4: 256 / S rows each, the keys shared out between S wave
+// groups), which take about 1 / S as long.  S is chosen to minimise the rounds of split
+// blocks, ceil(S rem / ncu) / S, in units of a whole tile's time (ties: fewer parts).  Only
+// where the tiles are of equal length (`may_split`: dense, non-causal).  A grid of fewer
+// tiles than CUs is not split: its key loops are short enough that the split blocks'
+// lockstep steps cost more than the idle CUs (1024-token shape: 27 -> 36 us).
 static void fwd_grid(FwdParams& p, int tiles, bool may_split, hipStream_t stream) {
   p.n_full = tiles;
   p.n_blocks = tiles;
-  if (!may_split) return;
+  p.split = 2;
+  if (!may_split || tiles == 0) return;
   const int ncu = cu_count(stream);
   const int rem = tiles % ncu;
-  if (tiles >= ncu && rem > 0 && 2 * rem <= ncu) {
+  if (tiles < ncu || rem == 0) return;
+  int best = 1;
+  double best_t = 1.0;
+  for (int S : {2, 4}) {
+    const double t = (double)cdiv((long)S * rem, ncu) / S;
+    if (t < best_t) {
+      best = S;
+      best_t = t;
+    }
+  }
+  if (best > 1) {
+    p.split = best;
     p.n_full = tiles - rem;
-    p.n_blocks = p.n_full + 2 * rem;
+    p.n_blocks = p.n_full + best * rem;
   }
 }
 

@@ -29,6 +29,8 @@
 //  * Split tail workgroups: when the grid's last round would fill at most half of
 //    the CUs, its query tiles run as pairs of 128-row workgroups whose wave groups
 //    share out the keys and combine their softmax states in LDS (see fwd_kernel).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -67,15 +69,15 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const bool grp_b = wave >= 4;
   const int hl = lane >> 5, l32 = lane & 31;
 
-  // Blocks from p.n_full on are split workgroups: the two halves (128 rows) of the query
-  // tiles n_full, n_full + 1, ..., each with its keys shared out between the two wave
-  // groups (see the split loop below).  They only exist for a non-causal dense launch whose
-  // last round of full workgroups would leave most CUs idle.
+  // Blocks from p.n_full on are split workgroups: the p.split parts (256 / p.split rows) of
+  // the query tiles n_full, n_full + 1, ..., each with its keys shared out between p.split
+  // wave groups (see the split loop below).  They only exist for a non-causal dense launch
+  // whose last round of full workgroups would leave most CUs idle.
   const bool split = (int)blockIdx.x >= p.n_full;
-  int qt, rest, half = 0;
+  int qt, rest, part = 0;
   if (split) {
-    const int b = (int)blockIdx.x - p.n_full, t = p.n_full + b / 2;
-    half = b & 1;
+    const int b = (int)blockIdx.x - p.n_full, t = p.n_full + b / p.split;
+    part = b % p.split;
     qt = t % p.n_qtiles;
     rest = t / p.n_qtiles;
   } else if (p.causal) {
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     lse_base = ((long)outer * p.H + head) * p.Sq;
     if (p.mask) mask = p.mask + (long)outer * p.Sk;
   }
-  const int qb = qt * BM + half * (BM / 2);  // first row of this workgroup
+  const int qb = qt * BM + (split ? part * (BM / p.split) : 0);  // first row of this workgroup
   if (qb >= nq) return;  // block-uniform
 
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const bf16* kbase = p.k + (long)krow0 * rsk + (long)kvh * D;
   const bf16* vbase = p.v + (long)krow0 * rsk + (long)kvh * D;
 
-  const int qw = qb + (split ? wave & 3 : wave) * 32;  // this wave's first query row
+  // this wave's first query row (a split workgroup holds 8 / p.split row blocks of 32)
+  const int qw = qb + (split ? wave % (8 / p.split) : wave) * 32;
   const int qrow = qw + l32;
   bf16x8 qreg[NKS];
   {
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   bf16x8 pk[2][2];
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = p.c2;
+  const std::integral_constant<int, 2> kTwoHalves{};
 
   const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
   const int ntiles = (kend + BN - 1) / BN;
@@ -167,14 +171,18 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 
   // Operand reads run several MFMAs ahead (explicit schedule): with one wave per SIMD in
   // its MFMA phase, nothing else hides an LDS read's latency from the matrix unit.
-  auto gemm_s = [&](const char* kt) __attribute__((always_inline)) {
-    sacc[0] = sacc[1] = f32x16{};
+  // kbc: the tile's number of 32-key halves (2, or 1 in the 32-key tiles of 4-way split
+  // workgroups), as a compile-time constant.
+  auto gemm_s = [&](const char* kt, auto kbc) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
         sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
-    constexpr int AHEAD = 6, N = 2 * NKS;
+    constexpr int AHEAD = 6, N = KB * NKS;
     ATTN_SCHED(kSchedDSRead, AHEAD);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -182,9 +190,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 1);
     }
   };
-  auto gemm_pv = [&](const char* vt) __attribute__((always_inline)) {
+  auto gemm_pv = [&](const char* vt, auto kbc) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
           const char* vb = vt + (32 * kb + 16 * t) * RB;
           oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
         }
-    constexpr int AHEAD = 4, N = 4 * NMB;  // MFMAs; two transposing reads each
+    constexpr int AHEAD = 4, N = 2 * KB * NMB;  // MFMAs; two transposing reads each
     ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -200,15 +209,17 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 2);
     }
   };
-  auto softmax = [&](int k0, uint64_t vw) __attribute__((always_inline)) {
-    if (vw != ~0ull || (p.causal && k0 + BN - 1 > qw)) {
+  auto softmax = [&](int k0, uint64_t vw, auto kbc) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value;
+    constexpr uint64_t kFull = KB == 2 ? ~0ull : 0xFFFFFFFFull;  // bits of the tile's keys
+    if ((vw & kFull) != kFull || (p.causal && k0 + 32 * KB - 1 > qw)) {
       keep_branch();
       // Register r of half kb holds key k0 + 32kb + 16(r/8) + 8hl + r%8 of row qrow.
       const uint64_t vl = vw >> (8 * hl);
       const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
       const int last = p.causal ? qrow - k0 - 8 * hl : BN;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kr = 32 * kb + 16 * (r >> 3) + (r & 7);
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     const float muse = m_run == -INFINITY ? 0.f : m_run;
     float la = 0.f, lb = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         f32x16 x;
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       keep_branch();
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = wave_max_halves(mx);
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       const float d = mnew == -INFINITY ? 0.f : mnew - muse;
       la = lb = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           f32x16 x;
@@ -277,10 +288,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // copies it issued in its previous phase.
   auto gemm_phase = [&](int j, const char* __restrict__ kt, const char* __restrict__ vp)
       __attribute__((always_inline)) {
-    if (vw_s != 0) gemm_pv(vp);  // vw_s: still the word of tile j-1
+    if (vw_s != 0) gemm_pv(vp, kTwoHalves);  // vw_s: still the word of tile j-1
     vw_s = tile_word(j, mbytes);
     mbytes = kv.load((j + 1) * BN);  // clamped: unused past the last tile
-    if (vw_s != 0) gemm_s(kt);
+    if (vw_s != 0) gemm_s(kt, kTwoHalves);
     if (grp_b) wait_tile_loads();
   };
   // VALU phase of tile j.  Group B first issues the copies of K(j+2) (into the buffer of
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if (j + 2 < ntiles) kld.issue(kn, kbase, rsk, (j + 2) * BN, nk);
       if (j + 1 < ntiles) vld.issue(vn, vbase, rsk, (j + 1) * BN, nk);
     }
-    if (vw_s != 0) softmax(j * BN, vw_s);
+    if (vw_s != 0) softmax(j * BN, vw_s, kTwoHalves);
   };
   // Both groups run the same sequence, group B one phase later (it passes one barrier
   // before its first phase, group A one after its last), so register lifetimes at every
@@ -304,53 +315,70 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     __syncthreads();
   };
 
-  if (split) {
-    // Split workgroup: both groups take the same 128 rows (wave w and w + 4 the same 32),
-    // group g the key tiles [g hn, (g + 1) hn), each with its own double-buffered K/V tiles
-    // and its own copies; both groups step in lockstep (one barrier per step).  The two
-    // partial softmax states are then combined through LDS.
-    const int g = grp_b ? 1 : 0;
-    const int hn = (ntiles + 1) / 2, t0 = g * hn, t1 = min(ntiles, t0 + hn);
-    char* const gb = smem + 4 * TILE * g;
-    TileLoader<D, BN, 4> gk, gv;
-    gk.init(rsk, krow, 4 * g);
-    gv.init(rsk, vrow, 4 * g);
+  // Split workgroup: p.split groups of 8 / p.split waves take the same 256 / p.split rows
+  // (wave w: row block w % (8 / p.split), group w / (8 / p.split)), group g the key tiles
+  // [g hn, (g + 1) hn), each group with its own double-buffered K/V tiles and its own copies
+  // (64-key tiles for two groups, 32-key tiles for four, so that every group's buffers fit);
+  // all groups step in lockstep (one barrier per step).  The partial softmax states are
+  // then combined through LDS.
+  auto split_run = [&](auto sc) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    constexpr int RBK = 8 / S;               // row blocks, and waves per group
+    constexpr int BNS = S == 2 ? 64 : 32;    // keys per tile
+    constexpr int TS = BNS * RB;             // bytes of one K or V tile
+    const std::integral_constant<int, BNS / 32> kb_c{};
+    const int g = wave / RBK;
+    const int nts = (kend + BNS - 1) / BNS;
+    const int hn = (nts + S - 1) / S, t0 = g * hn, t1 = min(nts, t0 + hn);
+    char* const gb = smem + 4 * TS * g;
+    TileLoader<D, BNS, RBK> gk, gv;
+    gk.init(rsk, krow, RBK * g);
+    gv.init(rsk, vrow, RBK * g);
+    auto word = [&](int j, uint32_t bytes) -> uint64_t __attribute__((always_inline)) {
+      if (j >= nts || (p.causal && j * BNS > qw + 31)) return 0;
+      return kv.word(j * BNS, bytes) & (BNS == 64 ? ~0ull : 0xFFFFFFFFull);
+    };
     uint64_t vw = 0;
     auto sstep = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt,
                      char* __restrict__ kn, char* __restrict__ vn) __attribute__((always_inline)) {
       const bool more = j + 1 < t1;
       uint64_t vw_next = 0;
       if (more) {
-        vw_next = tile_word(j + 1, mbytes);
-        mbytes = kv.load((j + 2) * BN);  // clamped: unused past the last tile
-        gk.issue(kn, kbase, rsk, (j + 1) * BN, nk);
-        gv.issue(vn, vbase, rsk, (j + 1) * BN, nk);
+        vw_next = word(j + 1, mbytes);
+        mbytes = kv.load((j + 2) * BNS);  // clamped: unused past the last tile
+        gk.issue(kn, kbase, rsk, (j + 1) * BNS, nk);
+        gv.issue(vn, vbase, rsk, (j + 1) * BNS, nk);
       }
       if (j < t1 && vw != 0) {
-        gemm_s(kt);
-        softmax(j * BN, vw);
-        gemm_pv(vt);
+        gemm_s(kt, kb_c);
+        softmax(j * BNS, vw, kb_c);
+        gemm_pv(vt, kb_c);
       }
       wait_tile_loads();
       __syncthreads();
       vw = vw_next;
     };
     if (t0 < t1) {
-      vw = tile_word(t0, kv.load(t0 * BN));
-      mbytes = kv.load((t0 + 1) * BN);
-      gk.issue(gb, kbase, rsk, t0 * BN, nk);
-      gv.issue(gb + 2 * TILE, vbase, rsk, t0 * BN, nk);
+      vw = word(t0, kv.load(t0 * BNS));
+      mbytes = kv.load((t0 + 1) * BNS);
+      gk.issue(gb, kbase, rsk, t0 * BNS, nk);
+      gv.issue(gb + 2 * TS, vbase, rsk, t0 * BNS, nk);
     }
     wait_tile_loads();
     __syncthreads();
     for (int s = 0; s < hn; s += 2) {
-      sstep(t0 + s, gb, gb + 2 * TILE, gb + TILE, gb + 3 * TILE);
-      if (s + 1 < hn) sstep(t0 + s + 1, gb + TILE, gb + 3 * TILE, gb, gb + 2 * TILE);
+      sstep(t0 + s, gb, gb + 2 * TS, gb + TS, gb + 3 * TS);
+      if (s + 1 < hn) sstep(t0 + s + 1, gb + TS, gb + 3 * TS, gb, gb + 2 * TS);
     }
-    // Combine: group B parks (m, l, O) per lane, group A merges and stores.
+    // Combine: groups 1.. park (m, l, O) per lane in LDS (every tile read has completed at
+    // the last step's barrier), group 0 merges them (m = max, each part scaled by 2^(m_g - m))
+    // and stores.
     l_run = wave_sum_halves(l_run);
-    float* red = reinterpret_cast<float*>(smem) + (wave & 3) * 64 * (16 * NMB + 2);
-    if (grp_b) {
+    constexpr int SLOT = 64 * (16 * NMB + 2);  // floats per parked wave
+    static_assert((S - 1) * RBK * SLOT * 4 <= 8 * TILE, "combine space");
+    const int rbk = wave % RBK;
+    if (g > 0) {
+      float* red = reinterpret_cast<float*>(smem) + ((g - 1) * RBK + rbk) * SLOT;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -359,17 +387,36 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       red[(16 * NMB + 1) * 64 + lane] = l_run;
     }
     __syncthreads();
-    if (grp_b) return;
-    const float mb_ = red[16 * NMB * 64 + lane], lb = red[(16 * NMB + 1) * 64 + lane];
-    const float m = fmaxf(m_run, mb_);
+    if (g > 0) return false;
+    float m = m_run;
+#pragma unroll
+    for (int gg = 1; gg < S; ++gg)
+      m = fmaxf(m, reinterpret_cast<const float*>(smem)[((gg - 1) * RBK + rbk) * SLOT + 16 * NMB * 64 + lane]);
     const float a = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    const float b = mb_ == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb_ - m);
+    l_run *= a;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[mb][r] = a * oacc[mb][r] + b * red[(mb * 16 + r) * 64 + lane];
-    l_run = a * l_run + b * lb;
+      for (int r = 0; r < 16; ++r) oacc[mb][r] *= a;
+#pragma unroll
+    for (int gg = 1; gg < S; ++gg) {
+      const float* red = reinterpret_cast<const float*>(smem) + ((gg - 1) * RBK + rbk) * SLOT;
+      const float mg = red[16 * NMB * 64 + lane];
+      const float b = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - m);
+      l_run += b * red[(16 * NMB + 1) * 64 + lane];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mb][r] += b * red[(mb * 16 + r) * 64 + lane];
+    }
     m_run = m;
+    return true;
+  };
+
+  if (split) {
+    const bool stores = p.split == 4 ? split_run(std::integral_constant<int, 4>{})
+                                     : split_run(std::integral_constant<int, 2>{});
+    if (!stores) return;
   } else {
   if (ntiles > 0) {
     mbytes = kv.load(0);

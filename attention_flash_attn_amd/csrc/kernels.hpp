@@ -29,7 +29,8 @@ struct FwdParams {
   int Hk, G;     // key/value heads and query heads per key/value head (H = G * Hk)
   int causal;    // query row i sees keys j <= i only (within its sequence)
   int n_qtiles;  // query tiles per (outer, head)
-  int n_full;    // blocks [0, n_full): whole query tiles; the rest: halves of tiles n_full...
+  int n_full;    // blocks [0, n_full): whole query tiles; the rest: parts of tiles n_full...
+  int split;     // parts (2 or 4) per query tile of the split blocks
   int n_blocks;
   float c2;  // scale * log2(e)
   SeqOrder order;  // varlen only

@@ -11,6 +11,14 @@ of every dO row); a bf16 output of magnitude m is itself only exact to 2^-8 * m,
 exceeds 2e-2 once m > 5, so for those cases the absolute part becomes
 2e-2 + 2^-8 * |oracle| per element (``quant_slack=True``).  The 1%-of-max part is kept.
 
+The absolute 2e-2 was set for the named workloads' softmax scale 1/sqrt(D), where the
+gradients stay below ~1.2.  A larger scale makes rows peakier and the gradients larger
+(scale 0.3 at D = 64: max |dQ| ~ 5), and the backward's delta, formed from the stored bf16
+out as the method prescribes, then differs from the oracle's (fp64 out) by up to
+sum_d |dO_d| 2^-9 |out_d| ~ 0.05, which moves dQ_i by scale * that * |(P K)_i| ~ 0.05 on its
+own.  Such synthetic-scale cases are held to the scale-free part of the bar, 1% of
+max|oracle| (``rel_only=True``), LSE unchanged.
+
 A tensor the oracle gives as identically zero is a gradient that cancels exactly (a
 query row that sees a single key has P = 1 and dP = delta, so its dS is 0 and so is the
 dK it feeds).  1% of its max would demand an exact zero from fp32 arithmetic that
@@ -43,14 +51,17 @@ def max_err(gpu, ref):
     return float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
 
 
-def assert_parity(name, gpu, ref, quant_slack=False):
+def assert_parity(name, gpu, ref, quant_slack=False, rel_only=False):
+    """rel_only: only the 1%-of-max part of the bar (see the module docstring on scales)."""
     assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
     if ref.size == 0:
         return
     assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
     err = max_err(gpu, ref)
     mx = float(np.max(np.abs(ref)))
-    if quant_slack:
+    if rel_only:
+        pass
+    elif quant_slack:
         excess = float(np.max(np.abs(gpu - ref) - (ABS_TOL + 2.0 ** -8 * np.abs(ref))))
         assert excess <= 0, f"{name}: error exceeds 2e-2 + 2^-8|ref| by {excess:.3e}"
     else:
