@@ -11,24 +11,24 @@
 //    S^T = K Q^T, so the score tile arrives with one query per lane and all
 //    row statistics (max, sum, LSE) are per-lane values; the only cross-lane
 //    step is one exchange between the two 32-lane halves.
-//  * K/V tiles of 64 keys are double-buffered in LDS and filled asynchronously
-//    by buffer loads into LDS.  Tiles are unpadded and XOR-swizzled (tile.hpp) so
-//    the row reads of K and the transposing reads of V are bank-conflict free.
-//    K rows are stored permuted (kRowPerm) so that the exponentiated score
+//  * K/V tiles of 64 keys are double- or triple-buffered in LDS and filled
+//    asynchronously by buffer loads into LDS.  Tiles are unpadded and XOR-swizzled
+//    (tile.hpp) so the row reads of K and the transposing reads of V are bank-conflict
+//    free.  K rows are stored permuted (kRowPerm) so that the exponentiated score
 //    registers are directly the B operand of O^T += V^T P^T.
 //  * Ping-pong: the two 4-wave groups (one wave of each per SIMD) run half a tile
 //    apart, so one group's MFMAs overlap the other group's softmax (see fwd_kernel).
-//  * Online softmax in base 2 with scale*log2(e) folded into one FMA.  The
-//    running max is only moved (and O, l rescaled) when the new tile max
-//    exceeds it by more than 8 (log2 units), so the rescale is rare; the
-//    unnormalised weights stay below 2^8 and the final division uses the
-//    same reference max, so the result is the same softmax.
+//  * Online softmax in base 2 with scale*log2(e) folded into one FMA, against a lazily
+//    moved reference: a tile's weights are formed against the row's current reference
+//    max, and the reference (with O and l rescaled) only moves when some row's tile sum
+//    exceeds 2^14, so every weight stays below 2^14 and the final division uses the same
+//    reference, which gives the same softmax.
 //  * Tiles whose keys are all masked are skipped; in partially valid tiles (a
 //    ragged tail or a mask edge) a branch taken only there sets the excluded
 //    scores to -inf, so full tiles carry no per-element mask work.
-//  * Split tail workgroups: when the grid's last round would fill at most half of
-//    the CUs, its query tiles run as pairs of 128-row workgroups whose wave groups
-//    share out the keys and combine their softmax states in LDS (see fwd_kernel).
+//  * Split tail workgroups: when the grid's last round would leave CUs idle, its query
+//    tiles run as two or four workgroups each whose wave groups share out the keys and
+//    combine their softmax states in LDS (see fwd_kernel).
 #include <type_traits>
 
 #include "common.hpp"
@@ -38,7 +38,9 @@
 namespace attn {
 
 // Waves 0..3 (group A) and 4..7 (group B) sit one per SIMD each (wave w and w + 4 share a
-// SIMD), so every SIMD holds one wave of each group.
+// SIMD), so every SIMD holds one wave of each group.  The loop below is the one for
+// masked and causal attention; dense attention runs a variant of it (dense_run) with a
+// fused MFMA phase and the copies shared between the groups.
 // The loop runs in phases separated by workgroup barriers, and the two groups are half a
 // key tile apart: in each phase one group issues its MFMAs (O += P V for the previous
 // tile, then S^T = K Q^T for the current one) while the other does the softmax VALU work,
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
                                         32 * mb + 16 * (g & 1) + 4 * (src & 3));
   }
 
-  TileLoader<D, BN, 4> kld, vld;  // used by group B only (waves 4..7)
+  TileLoader<D, BN, 4> kld, vld;  // the masked / causal loop: used by group B only
   auto krow = [](int r) { return perm32_row(r); };
   auto vrow = [](int r) { return r; };
   kld.init(rsk, krow, 4);
@@ -207,6 +209,36 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     for (int n = 0; n < N; ++n) {
       ATTN_SCHED(kSchedMFMA, 1);
       if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 2);
+    }
+  };
+  // O += P V of the previous tile, then S^T = K Q^T of this one, as one read pipeline: the
+  // first K reads issue under the last P V MFMAs, so the matrix unit does not wait for
+  // them between the two products.
+  auto gemm_pv_s = [&](const char* vt, const char* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const char* vb = vt + (32 * kb + 16 * t) * RB;
+          oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
+        }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
+    // MFMA n < NPV reads two transposed V fragments, the others one K row fragment.
+    constexpr int AHEAD = 4, NPV = 4 * NMB, N = NPV + 2 * NKS;
+    ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      ATTN_SCHED(kSchedMFMA, 1);
+      if (n + AHEAD < NPV) ATTN_SCHED(kSchedDSRead, 2);
+      else if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 1);
     }
   };
   auto softmax = [&](int k0, uint64_t vw, auto kbc) __attribute__((always_inline)) {
@@ -315,6 +347,86 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     __syncthreads();
   };
 
+  // Dense ping-pong (no mask, non-causal): every tile before the end is valid for every
+  // wave, so the MFMA phase of tile j is one read pipeline O += P(j-1) V(j-1), S(j)
+  // (gemm_pv_s), with the first (S(0) only) and last (P V only) phases peeled.  K(j) and V(j)
+  // sit in buffer j % 3 of each, and each group copies in its own VALU phase: group A
+  // K(j+2) during softmax(j) (phase 2j+1), group B V(j+1) during its softmax(j) (phase
+  // 2j+2), each waiting for its copies at the end of its next MFMA phase.  K(j+2) overwrites
+  // K(j-1), last read in phase 2j-1; V(j+1) overwrites V(j-2), last read in phase 2j-1;
+  // both are first read in phase 2j+4.  Splitting the copies halves the time a VALU phase
+  // spends issuing them, and the phase barriers do not wait for copies in flight.
+  // Dense ping-pong (no mask, non-causal): every tile before the end is valid for every
+  // wave, so the MFMA phase of tile j is one read pipeline O += P(j-1) V(j-1), S(j)
+  // (gemm_pv_s), with the first (S(0) only) and last (P V only) phases peeled.  K(j) and V(j)
+  // sit in buffer j % 3 of each, and each group copies in its own VALU phase: group A
+  // K(j+2) during softmax(j) (phase 2j+1), group B V(j+1) during its softmax(j) (phase
+  // 2j+2), each waiting for its copies at the end of its next MFMA phase.  K(j+2) overwrites
+  // K(j-1), last read in phase 2j-1; V(j+1) overwrites V(j-2), last read in phase 2j-1;
+  // both are first read in phase 2j+4.  Splitting the copies halves the time a VALU phase
+  // spends issuing them, and the phase barriers do not wait for copies in flight.
+  auto dense_run = [&]() __attribute__((always_inline)) {
+    char* const dK0 = smem;
+    char* const dK1 = smem + TILE;
+    char* const dK2 = smem + 2 * TILE;
+    char* const dV0 = smem + 3 * TILE;
+    char* const dV1 = smem + 4 * TILE;
+    char* const dV2 = smem + 5 * TILE;
+    // One loader per wave: group A copies K (rows permuted), group B copies V.  (Choosing
+    // between two loader objects per group would put them in scratch memory.)
+    TileLoader<D, BN, 4> cld;
+    cld.init(rsk, [&](int r) { return grp_b ? r : perm32_row(r); }, 4 * grp_b);
+    const bf16* const cbase = grp_b ? vbase : kbase;
+    const int lead = grp_b ? 1 : 2;  // group A copies K(j+2), group B V(j+1)
+    // A phase barrier that does not wait for copies in flight (__syncthreads() would).  Only
+    // register operations can move across it: the compiler may issue the last MFMAs of a
+    // phase after it, whose operands were read before it from buffers that the next phase
+    // does not overwrite (measured 0.4% faster than keeping them in front).
+    auto bar = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+    auto word = [&](int j) -> uint64_t __attribute__((always_inline)) { return kv.word(j * BN, 1u); };
+    // VALU phase of tile j (kn: the buffer of K(j+2), vn: the buffer of V(j+1))
+    auto vphase = [&](int j, char* __restrict__ kn, char* __restrict__ vn) __attribute__((always_inline)) {
+      if (j + lead < ntiles) cld.issue(grp_b ? vn : kn, cbase, rsk, (j + lead) * BN, nk);
+      softmax(j * BN, vw_s, kTwoHalves);
+    };
+    // pair of phases of tile j, 0 < j < ntiles (kt: K(j), vp: V(j-1))
+    auto dpair = [&](int j, const char* __restrict__ kt, const char* __restrict__ vp,
+                     char* __restrict__ kn, char* __restrict__ vn) __attribute__((always_inline)) {
+      gemm_pv_s(vp, kt);
+      vw_s = word(j);
+      wait_tile_loads();
+      bar();
+      vphase(j, kn, vn);
+      bar();
+    };
+    // K(0) and K(1) by group A, V(0) by group B, before the first phase
+    if (grp_b) {
+      cld.issue(dV0, vbase, rsk, 0, nk);
+    } else {
+      cld.issue(dK0, kbase, rsk, 0, nk);
+      if (1 < ntiles) cld.issue(dK1, kbase, rsk, BN, nk);
+    }
+    wait_tile_loads();
+    __syncthreads();
+    if (grp_b) bar();  // phase 0: group A forms S(0)
+    gemm_s(dK0, kTwoHalves);
+    vw_s = word(0);
+    wait_tile_loads();
+    bar();
+    vphase(0, dK2, dV1);
+    bar();
+    for (int j = 1; j < ntiles; j += 3) {  // j % 3 == 1, 2, 0
+      dpair(j, dK1, dV0, dK0, dV2);
+      if (j + 1 < ntiles) dpair(j + 1, dK2, dV1, dK1, dV0);
+      if (j + 2 < ntiles) dpair(j + 2, dK0, dV2, dK2, dV1);
+    }
+    // phase pair ntiles: O += P V of the last tile only
+    gemm_pv(smem + (3 + (ntiles - 1) % 3) * TILE, kTwoHalves);
+    bar();
+    bar();
+    if (!grp_b) bar();
+  };
+
   // Split workgroup: p.split groups of 8 / p.split waves take the same 256 / p.split rows
   // (wave w: row block w % (8 / p.split), group w / (8 / p.split)), group g the key tiles
   // [g hn, (g + 1) hn), each group with its own double-buffered K/V tiles and its own copies
@@ -417,6 +529,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     const bool stores = p.split == 4 ? split_run(std::integral_constant<int, 4>{})
                                      : split_run(std::integral_constant<int, 2>{});
     if (!stores) return;
+  } else if (!p.causal && !mask) {
+    if (ntiles > 0) dense_run();
+    l_run = wave_sum_halves(l_run);
   } else {
   if (ntiles > 0) {
     mbytes = kv.load(0);
