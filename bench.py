@@ -13,9 +13,10 @@ average duration inside the timed region; the dominant kernel's roofline line
 uses its own algorithmic FLOPs and that duration.  The fp64 CPU oracle is
 timed beside it on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--graph]
 (defaults: 10 warm-up and 50 timed steps; per-step median, min and mean are reported
-beside the mean-based value)
+beside the mean-based value; --graph times replays of one captured HIP graph of the step,
+which removes the launch gaps that dominate the small workloads)
 """
 from __future__ import annotations
 
@@ -51,6 +52,10 @@ def parse():
                     help="time the ring / context-parallel path instead: keys split into this "
                          "many chunks, per-chunk forwards merged by attn_lse_merge, per-chunk "
                          "backward with the merged statistics (attn_bwd_accum), fp32 -> bf16 casts")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one captured HIP graph of the step (the "
+                         "same three kernels without per-launch gaps); per-kernel times then "
+                         "come from the same number of eager steps run after the timed region")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling the profiler's HBM counters)")
@@ -310,17 +315,44 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    graph_ms = None
+    if args.graph:
+        # One step captured as a HIP graph (every output buffer preallocated, no memset in
+        # the captured calls), warmed up, then K replays timed between two events.
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        g0.record()
+        for _ in range(K):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ms = g0.elapsed_time(g1) / K
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t0e = time.perf_counter()
     for i in range(K):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if graph_ms is None:
+        wall = time.perf_counter() - t0e
     per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                     for e in evs])  # ms
     steps_each = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    step_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / K
+    eager_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / K
+    step_ms = graph_ms if graph_ms is not None else eager_ms
     fwd_ms, pre_ms, bwd_ms = (float(x) for x in per.mean(0))
 
     f_fwd = w.fwd_flops()
@@ -367,6 +399,9 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name, dom)},
     }
+    if graph_ms is not None:
+        res["step_mode"] = "hip graph replay (kernels_ms, step_ms_stats: eager steps)"
+        res["eager_ms_per_step"] = round(eager_ms, 4)
     res.update(calibration_copy(args.copy_calibration_mb))
     if not args.no_cpu_baseline and not w.varlen and w.valid_lens is None and not w.causal:
         res["cpu_baseline"] = cpu_baseline(w, t, min(args.cpu_rows, w.S))
