@@ -86,6 +86,8 @@ SMALL = [
     (2, 257, 257, 2, 64, (64, 200)),  # edge on a tile boundary and inside a tile
     (1, 1, 1, 1, 64, None),
     (1, 5, 700, 1, 128, None),
+    (1, 150, 170, 2, 128, None),      # 3 key tiles: the dense loop's second remainder pair
+    (2, 100, 190, 2, 64, None),
 ]
 
 
