@@ -52,6 +52,10 @@ def parse():
                     help="time the ring / context-parallel path instead: keys split into this "
                          "many chunks, per-chunk forwards merged by attn_lse_merge, per-chunk "
                          "backward with the merged statistics (attn_bwd_accum), fp32 -> bf16 casts")
+    ap.add_argument("--data", default="normal", choices=("normal", "zeros"),
+                    help="input values: normal (q, k, v, dO ~ N(0,1) rounded to bf16, the "
+                         "benchmark's data) or zeros (same shapes and work, minimal switching "
+                         "activity: shows how much of the time the power limit sets)")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of one captured HIP graph of the step (the "
                          "same three kernels without per-launch gaps); per-kernel times then "
@@ -268,6 +272,9 @@ def main():
     A.lib()
     w = I.WORKLOADS[args.workload]
     t = I.draw_workload(w)
+    if args.data == "zeros":
+        import dataclasses
+        t = dataclasses.replace(t, **{n: np.zeros_like(getattr(t, n)) for n in ("q", "k", "v", "do")})
     if args.ring_chunks > 0:
         res = run_ring(args, w, t, args.ring_chunks)
         res.update(calibration_copy(args.copy_calibration_mb))
@@ -375,7 +382,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": f"synthetic: q,k,v,dO ~ N(0,1) seed {w.seed}, rounded to bf16",
+        "data": (f"synthetic: q,k,v,dO ~ N(0,1) seed {w.seed}, rounded to bf16" if args.data == "normal"
+                 else "synthetic: q,k,v,dO all zero (power-limit diagnostic, not the metric's data)"),
         "config": {"workload": describe(w), "batch": B, "seq_len": S, "heads": H,
                    "head_dim": D, "parallelism": "none"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
