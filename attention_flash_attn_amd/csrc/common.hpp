@@ -1,6 +1,6 @@
 // common.hpp -- device helpers shared by the libattn kernels (gfx950 only).
 //
-// MFMA operand layouts used throughout (wave64, v_mfma_f32_32x32x16_bf16):
+// MFMA operand layouts of v_mfma_f32_32x32x16_bf16 (wave64; the backward's products):
 //   A (32 x 16):  lane l holds row l%32, reduction slots 8*(l/32) .. +7
 //   B (16 x 32):  lane l holds column l%32, reduction slots 8*(l/32) .. +7
 //   C (32 x 32):  lane l holds column l%32; register r holds row
@@ -36,6 +36,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16 (verified on the GPU with an in-bounds probe):
+//   A (16 x 32): lane l holds row l%16, reduction slots 8*(l/16) .. +7
+//   B (32 x 16): lane l holds column l%16, reduction slots 8*(l/16) .. +7
+//   C (16 x 16): lane l holds column l%16; register i holds row 4*(l/16) + i
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Row permutation inside a 32-row block: swaps bit 2 and bit 3 of the index.

@@ -7,22 +7,25 @@
 //
 // Design (one workgroup = 8 waves = 256 query rows of one (batch|sequence, head), one
 // workgroup per CU):
-//  * Each wave keeps its 32 query rows in registers as the B operand of
-//    S^T = K Q^T, so the score tile arrives with one query per lane and all
-//    row statistics (max, sum, LSE) are per-lane values; the only cross-lane
-//    step is one exchange between the two 32-lane halves.
+//  * Products on v_mfma_f32_16x16x32_bf16: under the package power limit this shape
+//    delivers more FLOP/s than the 32x32x16 one on random operands (half the accumulator
+//    traffic per multiply-add).  Each wave keeps its 32 query rows in registers as the B
+//    operands (two 16-query blocks) of S^T = K Q^T, so every lane holds two queries, and
+//    a query's scores are spread over four lanes (l, l^16, l^32, l^48); row statistics are
+//    per-lane partials, combined across the four lanes only where needed.
 //  * K/V tiles of 64 keys are double- or triple-buffered in LDS and filled
 //    asynchronously by buffer loads into LDS.  Tiles are unpadded and XOR-swizzled
-//    (tile.hpp) so the row reads of K and the transposing reads of V are bank-conflict
-//    free.  K rows are stored permuted (kRowPerm) so that the exponentiated score
-//    registers are directly the B operand of O^T += V^T P^T.
+//    (tile.hpp, the 16x16 swizzle) so the row reads of K and the transposing reads of V
+//    are bank-conflict free.  The score registers of a lane (keys 4g..4g+3 and 16+4g..
+//    16+4g+3 of each 32-key step, g = lane / 16) are directly the B operand of
+//    O^T += V^T P^T; the transposing reads of V fetch the same key order.
 //  * Ping-pong: the two 4-wave groups (one wave of each per SIMD) run half a tile
 //    apart, so one group's MFMAs overlap the other group's softmax (see fwd_kernel).
 //  * Online softmax in base 2 with scale*log2(e) folded into one FMA, against a lazily
 //    moved reference: a tile's weights are formed against the row's current reference
-//    max, and the reference (with O and l rescaled) only moves when some row's tile sum
-//    exceeds 2^14, so every weight stays below 2^14 and the final division uses the same
-//    reference, which gives the same softmax.
+//    max, and the reference (with O and l rescaled) only moves when some lane's partial
+//    tile sum of a row exceeds 2^14, so every weight stays below 2^14 and the final
+//    division uses the same reference, which gives the same softmax.
 //  * Tiles whose keys are all masked are skipped; in partially valid tiles (a
 //    ragged tail or a mask edge) a branch taken only there sets the excluded
 //    scores to -inf, so full tiles carry no per-element mask work.
@@ -55,8 +58,8 @@ template <int D, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = 64;
   constexpr int RB = 2 * D;
-  constexpr int NKS = D / 16;
-  constexpr int NMB = D / 32;
+  constexpr int NKS = D / 32;  // 32-wide reduction steps of S^T = K Q^T
+  constexpr int ND = D / 16;   // 16-row blocks of O^T
   constexpr int TILE = BN * RB;  // bytes of one K or V tile
   // Ping-pong workgroups use the first four tiles; a split workgroup (below) gives each
   // wave group four of its own.
@@ -69,7 +72,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool grp_b = wave >= 4;
-  const int hl = lane >> 5, l32 = lane & 31;
+  // 16x16x32 operand roles: lane = 16 g + c holds column / row c of a block and reduction
+  // slots 8g .. 8g+7; an output block gives it column c, rows 4g .. 4g+3.
+  const int g = lane >> 4, c = lane & 15;
 
   // Blocks from p.n_full on are split workgroups: the p.split parts (256 / p.split rows) of
   // the query tiles n_full, n_full + 1, ..., each with its keys shared out between p.split
@@ -113,52 +118,52 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     lse_base = ((long)outer * p.H + head) * p.Sq;
     if (p.mask) mask = p.mask + (long)outer * p.Sk;
   }
-  const int qb = qt * BM + (split ? part * (BM / p.split) : 0);  // first row of this workgroup
-  if (qb >= nq) return;  // block-uniform
+  const int q0w = qt * BM + (split ? part * (BM / p.split) : 0);  // first row of this workgroup
+  if (q0w >= nq) return;  // block-uniform
 
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int kvh = head / p.G;
   const bf16* kbase = p.k + (long)krow0 * rsk + (long)kvh * D;
   const bf16* vbase = p.v + (long)krow0 * rsk + (long)kvh * D;
 
-  // this wave's first query row (a split workgroup holds 8 / p.split row blocks of 32)
-  const int qw = qb + (split ? wave % (8 / p.split) : wave) * 32;
-  const int qrow = qw + l32;
-  bf16x8 qreg[NKS];
-  {
-    const bf16* qp = p.q + ((long)qrow0 + min(qrow, nq - 1)) * rs + (long)head * D + 8 * hl;
+  // this wave's first query row (a split workgroup holds 8 / p.split row blocks of 32); the
+  // lane's two queries are qw + c (block 0) and qw + 16 + c (block 1)
+  const int qw = q0w + (split ? wave % (8 / p.split) : wave) * 32;
+  bf16x8 qreg[2][NKS];  // [query block][step]: q[qw + 16 qb + c][32 ks + 8g .. +7]
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = as_bf16x8(ld16(qp + 16 * ks));
+  for (int qb = 0; qb < 2; ++qb) {
+    const bf16* qp = p.q + ((long)qrow0 + min(qw + 16 * qb + c, nq - 1)) * rs + (long)head * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qreg[qb][ks] = as_bf16x8(ld16(qp + 32 * ks));
   }
-  int koff[NKS], voff[NMB][2];
+  // K fragment of key block kb, step ks: tile row 16 kb + c, chunk 4 ks + g.  V^T fragment
+  // of d block db in a 32-key step: keys 4g + e (low half) and 16 + 4g + e (high half),
+  // e = 0..3, at d = 16 db + c (transposing reads; source lane 4e + t of a 16-lane group
+  // addresses row 4g + e (+16), columns 16 db + 4t .. +3).
+  int koff[NKS], voff[ND][2];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hl);
-  {
-    const int g = lane >> 4, src = lane & 15;
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D, true>(c, 4 * ks + g);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-        voff[mb][half] = tile_off_tr<D>(8 * (g >> 1) + 4 * half + (src >> 2),
-                                        32 * mb + 16 * (g & 1) + 4 * (src & 3));
-  }
+    for (int h = 0; h < 2; ++h)
+      voff[db][h] = tile_off_tr<D, true>(16 * h + 4 * g + (c >> 2), 16 * db + 4 * (c & 3));
 
-  TileLoader<D, BN, 4> kld, vld;  // the masked / causal loop: used by group B only
-  auto krow = [](int r) { return perm32_row(r); };
-  auto vrow = [](int r) { return r; };
-  kld.init(rsk, krow, 4);
-  vld.init(rsk, vrow, 4);
+  TileLoader<D, BN, 4, true> kld, vld;  // the masked / causal loop: used by group B only
+  auto same_row = [](int r) { return r; };
+  kld.init(rsk, same_row, 4);
+  vld.init(rsk, same_row, 4);
 
-  f32x16 oacc[NMB];
+  f32x4 oacc[ND][2];  // O^T block (d 16 db + 4g + i, query 16 qb + c)
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
-  f32x16 sacc[2];
-  bf16x8 pk[2][2];
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int db = 0; db < ND; ++db) oacc[db][0] = oacc[db][1] = f32x4{};
+  f32x4 sacc[4][2];   // S^T block (key 16 kb + 4g + i, query 16 qb + c)
+  bf16x8 pk[2][2];    // [32-key step][query block]: weights of keys 4g+i, 16+4g+i
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};  // per query; l: lane partial
   const float c2 = p.c2;
   const std::integral_constant<int, 2> kTwoHalves{};
 
-  const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
+  const int kend = p.causal ? min(nk, min(q0w + BM, nq)) : nk;
   const int ntiles = (kend + BN - 1) / BN;
   const KeyValidity kv{mask, nk};
   // Per wave: the key-validity word of the tile whose scores were formed last (0: nothing
@@ -176,39 +181,43 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // kbc: the tile's number of 32-key halves (2, or 1 in the 32-key tiles of 4-way split
   // workgroups), as a compile-time constant.
   auto gemm_s = [&](const char* kt, auto kbc) __attribute__((always_inline)) {
-    constexpr int KB = decltype(kbc)::value;
+    constexpr int NKB = 2 * decltype(kbc)::value;  // 16-key blocks
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb][0] = sacc[kb][1] = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
-    constexpr int AHEAD = 6, N = KB * NKS;
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 a = lds_row16(kt, kb * 16 * RB + koff[ks]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = mfma16(a, qreg[qb][ks], sacc[kb][qb]);
+      }
+    // one K fragment read per two MFMAs, issued AHEAD fragments early
+    constexpr int AHEAD = 3, R = NKS * NKB;
     ATTN_SCHED(kSchedDSRead, AHEAD);
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      ATTN_SCHED(kSchedMFMA, 1);
-      if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 1);
+    for (int n = 0; n < R; ++n) {
+      ATTN_SCHED(kSchedMFMA, 2);
+      if (n + AHEAD < R) ATTN_SCHED(kSchedDSRead, 1);
     }
   };
   auto gemm_pv = [&](const char* vt, auto kbc) __attribute__((always_inline)) {
-    constexpr int KB = decltype(kbc)::value;
+    constexpr int KB = decltype(kbc)::value;  // 32-key steps
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int s = 0; s < KB; ++s)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 a = lds_tr8(vt + 32 * s * RB, voff[db][0], voff[db][1]);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const char* vb = vt + (32 * kb + 16 * t) * RB;
-          oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
-        }
-    constexpr int AHEAD = 4, N = 2 * KB * NMB;  // MFMAs; two transposing reads each
+        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma16(a, pk[s][qb], oacc[db][qb]);
+      }
+    // two transposing reads per fragment, one fragment per two MFMAs
+    constexpr int AHEAD = 2, F = KB * ND;
     ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      ATTN_SCHED(kSchedMFMA, 1);
-      if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 2);
+    for (int n = 0; n < F; ++n) {
+      ATTN_SCHED(kSchedMFMA, 2);
+      if (n + AHEAD < F) ATTN_SCHED(kSchedDSRead, 2);
     }
   };
   // O += P V of the previous tile, then S^T = K Q^T of this one, as one read pipeline: the
@@ -216,105 +225,123 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // them between the two products.
   auto gemm_pv_s = [&](const char* vt, const char* kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 a = lds_tr8(vt + 32 * s * RB, voff[db][0], voff[db][1]);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const char* vb = vt + (32 * kb + 16 * t) * RB;
-          oacc[mb] = mfma32(lds_tr8(vb, voff[mb][0], voff[mb][1]), pk[kb][t], oacc[mb]);
-        }
+        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma16(a, pk[s][qb], oacc[db][qb]);
+      }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < 4; ++kb) sacc[kb][0] = sacc[kb][1] = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = mfma32(lds_row16(kt, kb * 32 * RB + koff[ks]), qreg[ks], sacc[kb]);
-    // MFMA n < NPV reads two transposed V fragments, the others one K row fragment.
-    constexpr int AHEAD = 4, NPV = 4 * NMB, N = NPV + 2 * NKS;
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a = lds_row16(kt, kb * 16 * RB + koff[ks]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = mfma16(a, qreg[qb][ks], sacc[kb][qb]);
+      }
+    // fragments f < F read two transposed V halves, the others one K row fragment; each
+    // feeds two MFMAs
+    constexpr int AHEAD = 2, F = 2 * ND, N = F + 4 * NKS;
     ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      ATTN_SCHED(kSchedMFMA, 1);
-      if (n + AHEAD < NPV) ATTN_SCHED(kSchedDSRead, 2);
+      ATTN_SCHED(kSchedMFMA, 2);
+      if (n + AHEAD < F) ATTN_SCHED(kSchedDSRead, 2);
       else if (n + AHEAD < N) ATTN_SCHED(kSchedDSRead, 1);
     }
   };
+  // Sum / max of a query's four lanes (l, l^16, l^32, l^48).
+  auto quad_sum = [](float x) __attribute__((always_inline)) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+  };
+  auto quad_max = [](float x) __attribute__((always_inline)) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+  };
   auto softmax = [&](int k0, uint64_t vw, auto kbc) __attribute__((always_inline)) {
-    constexpr int KB = decltype(kbc)::value;
+    constexpr int KB = decltype(kbc)::value, NKB = 2 * KB;
     constexpr uint64_t kFull = KB == 2 ? ~0ull : 0xFFFFFFFFull;  // bits of the tile's keys
     if ((vw & kFull) != kFull || (p.causal && k0 + 32 * KB - 1 > qw)) {
       keep_branch();
-      // Register r of half kb holds key k0 + 32kb + 16(r/8) + 8hl + r%8 of row qrow.
-      const uint64_t vl = vw >> (8 * hl);
-      const uint32_t w2[2] = {(uint32_t)vl, (uint32_t)(vl >> 32)};
-      const int last = p.causal ? qrow - k0 - 8 * hl : BN;
+      // value i of block (kb, qb) is key k0 + 16 kb + 4g + i of query qw + 16 qb + c
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = 32 * kb + 16 * (r >> 3) + (r & 7);
-          const bool on = ((w2[kb] >> (16 * (r >> 3) + (r & 7))) & 1u) && kr <= last;
-          sacc[kb][r] = on ? sacc[kb][r] : -INFINITY;
-        }
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kr = 16 * kb + 4 * g + i;
+            const bool on = ((vw >> kr) & 1u) && (!p.causal || k0 + kr <= qw + 16 * qb + c);
+            sacc[kb][qb][i] = on ? sacc[kb][qb][i] : -INFINITY;
+          }
     }
-    // Weights against the row's current reference m_run, with no max over the tile: the
-    // exponent arguments y = c2 s - m_run stay in sacc, and the tile is accepted unless some
-    // row's tile sum exceeds 2^14 (or overflows), which keeps every weight below 2^14.  The
-    // first tile of a row (no reference yet) and the rare rejected tile form the tile max
-    // from y, move the reference up by it, rescale O and l, and recompute the weights.
-    const bool first = __ballot(m_run == -INFINITY) != 0;
-    const float muse = m_run == -INFINITY ? 0.f : m_run;
-    float la = 0.f, lb = 0.f;
+    // Weights against the rows' current references m_run, with no max over the tile: the
+    // exponent arguments y = c2 s - m stay in sacc, and the tile is accepted unless some
+    // lane's partial sum of a row exceeds 2^14 (or overflows), which keeps every weight
+    // below 2^14.  The first tile of a row (no reference yet) and the rare rejected tile
+    // form the tile max from y (over the row's four lanes), move the reference up by it,
+    // rescale O and l, and recompute the weights.
+    const bool first = __ballot(m_run[0] == -INFINITY || m_run[1] == -INFINITY) != 0;
+    float muse[2], lt[2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+      muse[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      lt[qb] = 0.f;
+    }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+    for (int s = 0; s < KB; ++s)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
         f32x16 x;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float y = fmaf(sacc[kb][8 * h + r], c2, -muse);
-          sacc[kb][8 * h + r] = y;
-          x[r] = __builtin_amdgcn_exp2f(y);
-          if (r & 1) lb += x[r]; else la += x[r];
-        }
-        pk[kb][h] = pack8(x, 0);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = fmaf(sacc[2 * s + h][qb][i], c2, -muse[qb]);
+            sacc[2 * s + h][qb][i] = y;
+            x[4 * h + i] = __builtin_amdgcn_exp2f(y);
+            lt[qb] += x[4 * h + i];
+          }
+        pk[s][qb] = pack8(x, 0);
       }
-    float lt = la + lb;
-    if (first || __ballot(!(lt <= 0x1p14f))) {
+    if (first || __ballot(!(lt[0] <= 0x1p14f) || !(lt[1] <= 0x1p14f))) {
       keep_branch();
-      float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = wave_max_halves(mx);
-      const float mnew = fmaxf(m_run, muse + mx);
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-      l_run *= alpha;
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
+        mx = quad_max(mx);
+        const float mnew = fmaxf(m_run[qb], muse[qb] + mx);
+        const float alpha = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+        l_run[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-      m_run = mnew;
-      const float d = mnew == -INFINITY ? 0.f : mnew - muse;
-      la = lb = 0.f;
+        for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha;
+        m_run[qb] = mnew;
+        const float d = mnew == -INFINITY ? 0.f : mnew - muse[qb];
+        lt[qb] = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int s = 0; s < KB; ++s) {
           f32x16 x;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            x[r] = __builtin_amdgcn_exp2f(sacc[kb][8 * h + r] - d);
-            if (r & 1) lb += x[r]; else la += x[r];
-          }
-          pk[kb][h] = pack8(x, 0);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[4 * h + i] = __builtin_amdgcn_exp2f(sacc[2 * s + h][qb][i] - d);
+              lt[qb] += x[4 * h + i];
+            }
+          pk[s][qb] = pack8(x, 0);
         }
-      lt = la + lb;
+      }
     }
-    l_run += lt;
+    l_run[0] += lt[0];
+    l_run[1] += lt[1];
   };
   // MFMA phase of tile j: O += P(j-1) V(j-1), then S(j).  Group B then waits for the
   // copies it issued in its previous phase.
@@ -356,15 +383,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // K(j-1), last read in phase 2j-1; V(j+1) overwrites V(j-2), last read in phase 2j-1;
   // both are first read in phase 2j+4.  Splitting the copies halves the time a VALU phase
   // spends issuing them, and the phase barriers do not wait for copies in flight.
-  // Dense ping-pong (no mask, non-causal): every tile before the end is valid for every
-  // wave, so the MFMA phase of tile j is one read pipeline O += P(j-1) V(j-1), S(j)
-  // (gemm_pv_s), with the first (S(0) only) and last (P V only) phases peeled.  K(j) and V(j)
-  // sit in buffer j % 3 of each, and each group copies in its own VALU phase: group A
-  // K(j+2) during softmax(j) (phase 2j+1), group B V(j+1) during its softmax(j) (phase
-  // 2j+2), each waiting for its copies at the end of its next MFMA phase.  K(j+2) overwrites
-  // K(j-1), last read in phase 2j-1; V(j+1) overwrites V(j-2), last read in phase 2j-1;
-  // both are first read in phase 2j+4.  Splitting the copies halves the time a VALU phase
-  // spends issuing them, and the phase barriers do not wait for copies in flight.
   auto dense_run = [&]() __attribute__((always_inline)) {
     char* const dK0 = smem;
     char* const dK1 = smem + TILE;
@@ -372,10 +390,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     char* const dV0 = smem + 3 * TILE;
     char* const dV1 = smem + 4 * TILE;
     char* const dV2 = smem + 5 * TILE;
-    // One loader per wave: group A copies K (rows permuted), group B copies V.  (Choosing
-    // between two loader objects per group would put them in scratch memory.)
-    TileLoader<D, BN, 4> cld;
-    cld.init(rsk, [&](int r) { return grp_b ? r : perm32_row(r); }, 4 * grp_b);
+    // One loader per wave: group A copies K, group B copies V.  (Choosing between two loader
+    // objects per group would put them in scratch memory.)
+    TileLoader<D, BN, 4, true> cld;
+    cld.init(rsk, same_row, 4 * grp_b);
     const bf16* const cbase = grp_b ? vbase : kbase;
     const int lead = grp_b ? 1 : 2;  // group A copies K(j+2), group B V(j+1)
     // A phase barrier that does not wait for copies in flight (__syncthreads() would).  Only
@@ -439,13 +457,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     constexpr int BNS = S == 2 ? 64 : 32;    // keys per tile
     constexpr int TS = BNS * RB;             // bytes of one K or V tile
     const std::integral_constant<int, BNS / 32> kb_c{};
-    const int g = wave / RBK;
+    const int grp = wave / RBK;
     const int nts = (kend + BNS - 1) / BNS;
-    const int hn = (nts + S - 1) / S, t0 = g * hn, t1 = min(nts, t0 + hn);
-    char* const gb = smem + 4 * TS * g;
-    TileLoader<D, BNS, RBK> gk, gv;
-    gk.init(rsk, krow, RBK * g);
-    gv.init(rsk, vrow, RBK * g);
+    const int hn = (nts + S - 1) / S, t0 = grp * hn, t1 = min(nts, t0 + hn);
+    char* const gb = smem + 4 * TS * grp;
+    TileLoader<D, BNS, RBK, true> gk, gv;
+    gk.init(rsk, same_row, RBK * grp);
+    gv.init(rsk, same_row, RBK * grp);
     auto word = [&](int j, uint32_t bytes) -> uint64_t __attribute__((always_inline)) {
       if (j >= nts || (p.causal && j * BNS > qw + 31)) return 0;
       return kv.word(j * BNS, bytes) & (BNS == 64 ? ~0ull : 0xFFFFFFFFull);
@@ -484,44 +502,51 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     }
     // Combine: groups 1.. park (m, l, O) per lane in LDS (every tile read has completed at
     // the last step's barrier), group 0 merges them (m = max, each part scaled by 2^(m_g - m))
-    // and stores.
-    l_run = wave_sum_halves(l_run);
-    constexpr int SLOT = 64 * (16 * NMB + 2);  // floats per parked wave
+    // and stores.  l stays a per-lane partial here (the same lanes of every group hold the
+    // same queries); it is summed over a query's four lanes afterwards.
+    constexpr int NO = ND * 8;               // O values per lane
+    constexpr int SLOT = 64 * (NO + 4);      // floats per parked wave
     static_assert((S - 1) * RBK * SLOT * 4 <= 8 * TILE, "combine space");
     const int rbk = wave % RBK;
-    if (g > 0) {
-      float* red = reinterpret_cast<float*>(smem) + ((g - 1) * RBK + rbk) * SLOT;
+    if (grp > 0) {
+      float* red = reinterpret_cast<float*>(smem) + ((grp - 1) * RBK + rbk) * SLOT;
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[(mb * 16 + r) * 64 + lane] = oacc[mb][r];
-      red[16 * NMB * 64 + lane] = m_run;
-      red[(16 * NMB + 1) * 64 + lane] = l_run;
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((db * 2 + qb) * 4 + i) * 64 + lane] = oacc[db][qb][i];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        red[(NO + qb) * 64 + lane] = m_run[qb];
+        red[(NO + 2 + qb) * 64 + lane] = l_run[qb];
+      }
     }
     __syncthreads();
-    if (g > 0) return false;
-    float m = m_run;
+    if (grp > 0) return false;
 #pragma unroll
-    for (int gg = 1; gg < S; ++gg)
-      m = fmaxf(m, reinterpret_cast<const float*>(smem)[((gg - 1) * RBK + rbk) * SLOT + 16 * NMB * 64 + lane]);
-    const float a = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    l_run *= a;
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = m_run[qb];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+      for (int gg = 1; gg < S; ++gg)
+        m = fmaxf(m, reinterpret_cast<const float*>(smem)[((gg - 1) * RBK + rbk) * SLOT + (NO + qb) * 64 + lane]);
+      const float a = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+      l_run[qb] *= a;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[mb][r] *= a;
+      for (int db = 0; db < ND; ++db) oacc[db][qb] *= a;
 #pragma unroll
-    for (int gg = 1; gg < S; ++gg) {
-      const float* red = reinterpret_cast<const float*>(smem) + ((gg - 1) * RBK + rbk) * SLOT;
-      const float mg = red[16 * NMB * 64 + lane];
-      const float b = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - m);
-      l_run += b * red[(16 * NMB + 1) * 64 + lane];
+      for (int gg = 1; gg < S; ++gg) {
+        const float* red = reinterpret_cast<const float*>(smem) + ((gg - 1) * RBK + rbk) * SLOT;
+        const float mg = red[(NO + qb) * 64 + lane];
+        const float b = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - m);
+        l_run[qb] += b * red[(NO + 2 + qb) * 64 + lane];
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mb][r] += b * red[(mb * 16 + r) * 64 + lane];
+          for (int i = 0; i < 4; ++i) oacc[db][qb][i] += b * red[((db * 2 + qb) * 4 + i) * 64 + lane];
+      }
+      m_run[qb] = m;
     }
-    m_run = m;
     return true;
   };
 
@@ -531,7 +556,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     if (!stores) return;
   } else if (!p.causal && !mask) {
     if (ntiles > 0) dense_run();
-    l_run = wave_sum_halves(l_run);
   } else {
   if (ntiles > 0) {
     mbytes = kv.load(0);
@@ -552,23 +576,26 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     }
     if (!grp_b) __syncthreads();
   }
-  l_run = wave_sum_halves(l_run);
   }
 
-  if (qrow < nq) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    bf16* op = p.out + ((long)qrow0 + qrow) * rs + (long)head * D + 4 * hl;
+  // l over each query's four lanes; lane (c, g) stores d = 16 db + 4g .. +3 of its two rows
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = quad_sum(l_run[qb]);
+    const int qrow = qw + 16 * qb + c;
+    if (qrow < nq) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16* op = p.out + ((long)qrow0 + qrow) * rs + (long)head * D + 4 * g;
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
+      for (int db = 0; db < ND; ++db) {
         bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[mb][4 * j4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * j4) = o;
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[db][qb][e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 16 * db) = o;
       }
-    if (hl == 0)
-      p.lse[lse_base + qrow] = l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+      if (g == 0)
+        p.lse[lse_base + qrow] = l > 0.f ? (m_run[qb] + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+    }
   }
 }
 
