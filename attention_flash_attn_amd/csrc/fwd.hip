@@ -193,7 +193,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = mfma16(a, qreg[qb][ks], sacc[kb][qb]);
       }
     // one K fragment read per two MFMAs, issued AHEAD fragments early
-    constexpr int AHEAD = 3, R = NKS * NKB;
+    constexpr int AHEAD = 5, R = NKS * NKB;
     ATTN_SCHED(kSchedDSRead, AHEAD);
 #pragma unroll
     for (int n = 0; n < R; ++n) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma16(a, pk[s][qb], oacc[db][qb]);
       }
     // two transposing reads per fragment, one fragment per two MFMAs
-    constexpr int AHEAD = 2, F = KB * ND;
+    constexpr int AHEAD = 3, F = KB * ND;
     ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
 #pragma unroll
     for (int n = 0; n < F; ++n) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       }
     // fragments f < F read two transposed V halves, the others one K row fragment; each
     // feeds two MFMAs
-    constexpr int AHEAD = 2, F = 2 * ND, N = F + 4 * NKS;
+    constexpr int AHEAD = 3, F = 2 * ND, N = F + 4 * NKS;
     ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
