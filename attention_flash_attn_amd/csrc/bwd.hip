@@ -21,10 +21,12 @@
 // S = Q K^T) and both 32-row halves of every tile, with its dK^T, dV^T accumulators in
 // registers across the loop.  Q^T and dO^T operands come from the LDS transposing read.
 //
-// dQ workgroup: 8 waves, 256 query rows; each wave keeps its 32 rows of Q and dO (B
-// operands of S^T = K Q^T and dP^T = V dO^T: one query per lane, so LSE and delta are
-// per-lane scalars) and its dQ^T accumulator in registers; K/V tiles of 64 keys are
-// double-buffered in LDS the same way; K^T comes from the transposing read.
+// dQ workgroup: 8 waves, 256 query rows, products on v_mfma_f32_16x16x32_bf16 (more
+// FLOP/s than 32x32x16 under the power limit); each wave keeps its 32 rows of Q and dO
+// (B operands of S^T = K Q^T and dP^T = V dO^T in two 16-query blocks: two queries per
+// lane, so LSE and delta are per-lane scalars) and its dQ^T accumulator in registers; K/V
+// tiles of 64 keys are double-buffered in LDS the same way (the 16x16 swizzle, natural row
+// order); K^T comes from the transposing read, in the key order of the lane's dS values.
 //
 // Eight waves, two per SIMD, keep each wave within 256 registers, so that one wave's
 // matrix instructions run while the other does its exponentials and conversions (a wave
@@ -446,67 +448,74 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
                                          int half) {
   constexpr int BM = 256, BN = DqSmem<D>::BN;
   constexpr int RB = 2 * D;
-  constexpr int NKS = D / 16, NMB = D / 32;
+  constexpr int NKS = D / 32, ND = D / 16;
   constexpr int GB = sizeof(DqSmem<D>);  // LDS distance between the wave groups' tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-  const int hl = lane >> 5, l32 = lane & 31;
+  // 16x16x32 operand roles: lane = 16 g + c holds column / row c of a block and reduction
+  // slots 8g .. 8g+7; an output block gives it column c, rows 4g .. 4g+3.
+  const int g = lane >> 4, c = lane & 15;
   const bool split = half >= 0;
   const int grp = split ? wave >> 2 : 0;
   // Causal: the last query tiles see the most keys, so they are dealt out first.
-  const int qb = (p.causal ? p.n_q_tiles - 1 - sl.tile : sl.tile) * BM + (split ? half * (BM / 2) : 0);
-  if (qb >= sl.nq) return;  // block-uniform
+  const int qb0 = (p.causal ? p.n_q_tiles - 1 - sl.tile : sl.tile) * BM + (split ? half * (BM / 2) : 0);
+  if (qb0 >= sl.nq) return;  // block-uniform
   // Q/dO/dQ rows hold H heads, K/V rows Hk (this query head reads key/value head kvhead).
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int nq = sl.nq, nk = sl.nk;
 
-  const int qrow = qb + (split ? wave & 3 : wave) * 32 + l32;
-  bf16x8 qreg[NKS], doreg[NKS];
-  {
-    const long off = ((long)sl.qrow0 + min(qrow, nq - 1)) * rs + (long)sl.qhead * D + 8 * hl;
+  // The wave's 32 rows; the lane's two queries are qw + c (block 0) and qw + 16 + c (block 1).
+  const int qw = qb0 + (split ? wave & 3 : wave) * 32;
+  bf16x8 qreg[2][NKS], doreg[2][NKS];  // [query block][step]: row qw + 16 qb + c, d 32 ks + 8g ..
+  float lse2[2], ndl[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw + 16 * qb + c;
+    const long off = ((long)sl.qrow0 + min(qrow, nq - 1)) * rs + (long)sl.qhead * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qreg[ks] = as_bf16x8(ld16(p.q + off + 16 * ks));
-      doreg[ks] = as_bf16x8(ld16(p.dout + off + 16 * ks));
+      qreg[qb][ks] = as_bf16x8(ld16(p.q + off + 32 * ks));
+      doreg[qb][ks] = as_bf16x8(ld16(p.dout + off + 32 * ks));
     }
+    // Rows past the end, and rows with no key to attend to (LSE = -inf: every visible key
+    // masked), take +inf so that P = exp2(c2 S - lse2) is 0 even where S is -inf.
+    const float lse_row = qrow < nq ? p.lse[sl.lse_base + qrow] : -INFINITY;
+    lse2[qb] = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
+    ndl[qb] = qrow < nq ? -p.delta[sl.lse_base + qrow] : 0.f;
   }
-  // Rows past the end, and rows with no key to attend to (LSE = -inf: every visible key
-  // masked), take +inf so that P = exp2(c2 S - lse2) is 0 even where S is -inf.
-  const float lse_row = qrow < nq ? p.lse[sl.lse_base + qrow] : -INFINITY;
-  const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
-  const float dl = qrow < nq ? p.delta[sl.lse_base + qrow] : 0.f;
+  // The dP^T accumulators start from the row's -delta (their C operand).
+  f32x4 ndl4[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) ndl4[qb] = f32x4{ndl[qb], ndl[qb], ndl[qb], ndl[qb]};
 
-  // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
-  // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
-  // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt at every step from the step-0
-  // offsets (3 registers instead of 16 held through the loop).  The offsets also carry the
-  // wave group's distance to its own tiles (GB, a multiple of 256 bytes, which the XORs
-  // leave alone), so the tile addresses stay constants.
-  int koff0 = tile_off<D>(l32, hl) + grp * GB, tr0[2];
-  {
-    int troff[NMB][2];
-    perm_tr_offsets<D>(lane, troff);
-    tr0[0] = troff[0][0] + grp * GB;
-    tr0[1] = troff[0][1] + grp * GB;
-  }
-  int koff[NKS], troff[NMB][2];
+  // LDS offsets.  K/V fragment of key block kb, step ks: tile row 16 kb + c, chunk 4 ks + g;
+  // K^T fragment of d block db in a 32-key step: keys 4g + e and 16 + 4g + e at d = 16 db + c
+  // (transposing reads).  Steps differ only in chunk bits, offset(ks) = offset(0) ^ 64 ks and
+  // offset(db) = offset(0) ^ 32 db (tile.hpp swizzle), so they are rebuilt at every step from
+  // the step-0 offsets (3 registers held through the loop).  The offsets also carry the wave
+  // group's distance to its own tiles (GB, a multiple of 256 bytes, which the XORs leave
+  // alone), so the tile addresses stay constants.
+  int koff0 = tile_off<D, true>(c, g) + grp * GB, tr0[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) tr0[h] = tile_off_tr<D, true>(16 * h + 4 * g + (c >> 2), 4 * (c & 3)) + grp * GB;
+  int koff[NKS], troff[ND][2];
   auto offsets = [&]() {
     asm volatile("" : "+v"(koff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) koff[ks] = koff0 ^ (32 * ks);
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = koff0 ^ (64 * ks);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      troff[mb][0] = tr0[0] ^ (64 * mb);
-      troff[mb][1] = tr0[1] ^ (64 * mb);
+    for (int db = 0; db < ND; ++db) {
+      troff[db][0] = tr0[0] ^ (32 * db);
+      troff[db][1] = tr0[1] ^ (32 * db);
     }
   };
 
   const bf16* kbase = p.k + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
-  auto krow_of = [](int r) { return perm32_row(r); };
-  TileLoader<D, BN, 4> ld;  // used by waves 0..3 (split: each group's four waves)
-  ld.init(rsk, krow_of, 4 * grp);
+  auto same_row = [](int r) { return r; };
+  TileLoader<D, BN, 4, true> ld;  // used by waves 0..3 (split: each group's four waves)
+  ld.init(rsk, same_row, 4 * grp);
   // Only waves 0..3 copy (see dkdv_block): while they stall at issue, waves 4..7, one per
   // SIMD, keep the matrix units busy.  In a split workgroup each group copies its own tiles.
   auto issue = [&](int k0, char* kt, char* vt) {
@@ -516,62 +525,83 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
     }
   };
 
-  f32x16 dqacc[NMB];
+  f32x4 dqacc[ND][2];  // dQ^T block (d 16 db + 4g + i, query 16 qb + c)
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
+  for (int db = 0; db < ND; ++db) dqacc[db][0] = dqacc[db][1] = f32x4{};
   const float c2 = p.c2;
-  // The dP^T accumulators start from the row's -delta (16 registers held through the loop,
-  // 32 subtractions a step fewer).
-  f32x16 ndl16;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
 
-  // Per 32-key half kb of a tile: scores A (S^T, dP^T MFMAs), weights B (VALU: P,
-  // dS), gradient C (dQ^T MFMAs), issued as A0 | A1 B0 | C0 B1 | C1 with hard
-  // scheduling boundaries.  Partial tiles mask the scores (to -inf) between the groups.
-  auto scores = [&](const char* kt, const char* vt, int kb, f32x16& st, f32x16& dpt) {
-    const int rb = kb * 32 * RB;
-    st = f32x16{};
-    dpt = ndl16;
+  // Per 32-key half h of a tile: scores A (S^T, dP^T MFMAs over key blocks 2h, 2h+1),
+  // weights B (VALU: P, dS), gradient C (dQ^T MFMAs), issued as A0 | A1 B0 | C0 B1 | C1 with
+  // hard scheduling boundaries.  Partial tiles mask the scores (to -inf) between the groups.
+  // st[b][qb], dpt[b][qb]: key block 2h + b, query block qb.
+  auto scores = [&](const char* kt, const char* vt, int h, f32x4 (&st)[2][2], f32x4 (&dpt)[2][2]) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) st = mfma32(lds_row16(kt, rb + koff[ks]), qreg[ks], st);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) dpt = mfma32(lds_row16(vt, rb + koff[ks]), doreg[ks], dpt);
-  };
-  auto mask_scores = [&](uint64_t vw, int k0, int kb, f32x16& st) {
-    // register r's key is k0 + 32kb + 16(r/8) + 8hl + r%8 (bit 32kb + 16(r/8) + 8hl + r%8 of
-    // vw); causal: visible only up to this lane's query row
-    const uint32_t w = (uint32_t)((vw >> (8 * hl)) >> (32 * kb));
-    const int last = p.causal ? qrow - k0 - 32 * kb - 8 * hl : BN;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool on = ((w >> (16 * (r >> 3) + (r & 7))) & 1u) && 16 * (r >> 3) + (r & 7) <= last;
-      st[r] = on ? st[r] : -INFINITY;
+    for (int b = 0; b < 2; ++b) {
+      st[b][0] = st[b][1] = f32x4{};
+      dpt[b][0] = ndl4[0];
+      dpt[b][1] = ndl4[1];
     }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bf16x8 a = lds_row16(kt, (2 * h + b) * 16 * RB + koff[ks]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) st[b][qb] = mfma16(a, qreg[qb][ks], st[b][qb]);
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bf16x8 a = lds_row16(vt, (2 * h + b) * 16 * RB + koff[ks]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dpt[b][qb] = mfma16(a, doreg[qb][ks], dpt[b][qb]);
+      }
+  };
+  auto mask_scores = [&](uint64_t vw, int k0, int h, f32x4 (&st)[2][2]) {
+    // value i of block (b, qb) is key k0 + 32h + 16b + 4g + i of query qw + 16 qb + c;
+    // causal: visible only up to the query's row
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = 32 * h + 16 * b + 4 * g + i;
+          const bool on = ((vw >> kr) & 1u) && (!p.causal || k0 + kr <= qw + 16 * qb + c);
+          st[b][qb][i] = on ? st[b][qb][i] : -INFINITY;
+        }
   };
   // Tiles that need per-element masking: not every key valid, or (causal) some key of the
   // tile after some query row of the workgroup.
-  auto needs_mask = [&](int k0, uint64_t vw) { return vw != ~0ull || (p.causal && k0 + BN - 1 > qb); };
-  auto weights = [&](f32x16& st, f32x16& dpt, bf16x8 (&ds)[2]) {
+  auto needs_mask = [&](int k0, uint64_t vw) { return vw != ~0ull || (p.causal && k0 + BN - 1 > qb0); };
+  // P = exp2(c2 S - lse2), dS = P (dP - delta); ds[qb]: the B operand of the dQ^T step (keys
+  // 4g + i of block 2h, then of block 2h + 1)
+  auto weights = [&](f32x4 (&st)[2][2], f32x4 (&dpt)[2][2], bf16x8 (&ds)[2]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
-      dpt[r] = st[r] * dpt[r];
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 x;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pw = __builtin_amdgcn_exp2f(fmaf(st[b][qb][i], c2, -lse2[qb]));
+          x[4 * b + i] = pw * dpt[b][qb][i];
+        }
+      ds[qb] = pack8(x, 0);
     }
-    ds[0] = pack8(dpt, 0);
-    ds[1] = pack8(dpt, 8);
   };
-  auto grad = [&](const char* kt, int kb, const bf16x8 (&ds)[2]) {
-    const int rb = kb * 32 * RB;
+  auto grad = [&](const char* kt, int h, const bf16x8 (&ds)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      dqacc[mb] = mfma32(lds_tr8(kt + rb, troff[mb][0], troff[mb][1]), ds[0], dqacc[mb]);
-      dqacc[mb] = mfma32(lds_tr8(kt + rb + 16 * RB, troff[mb][0], troff[mb][1]), ds[1], dqacc[mb]);
+    for (int db = 0; db < ND; ++db) {
+      const bf16x8 a = lds_tr8(kt + 32 * h * RB, troff[db][0], troff[db][1]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) dqacc[db][qb] = mfma16(a, ds[qb], dqacc[db][qb]);
     }
   };
   auto compute = [&](const char* kt, const char* vt, int k0, uint64_t vw) {
     offsets();
-    f32x16 st0, dpt0, st1, dpt1;
+    f32x4 st0[2][2], dpt0[2][2], st1[2][2], dpt1[2][2];
     bf16x8 ds0[2], ds1[2];
     scores(kt, vt, 0, st0, dpt0);
     const bool masked = needs_mask(k0, vw);
@@ -598,7 +628,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   };
 
   // Causal: keys past the workgroup's last query row are never seen.
-  const int kend = p.causal ? min(nk, min(qb + BM, nq)) : nk;
+  const int kend = p.causal ? min(nk, min(qb0 + BM, nq)) : nk;
   const int ntiles = (kend + BN - 1) / BN;
   // This wave group's key tiles [t0, t1), hn steps (a split workgroup's groups step in
   // lockstep, one barrier per step; a group past its last tile only takes the barriers).
@@ -636,40 +666,44 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   if (split) {
     // Group 1 parks its partial sums in LDS (every tile read has completed at the last
     // step's barrier), group 0 adds them and stores.
-    static_assert(4 * NMB * 16 * 64 * sizeof(float) <= 2 * sizeof(DqSmem<D>), "reduction space");
-    float* red = reinterpret_cast<float*>(&sm[0]) + (wave & 3) * (NMB * 16 * 64);
+    static_assert(4 * ND * 8 * 64 * sizeof(float) <= 2 * sizeof(DqSmem<D>), "reduction space");
+    float* red = reinterpret_cast<float*>(&sm[0]) + (wave & 3) * (ND * 8 * 64);
     if (grp == 1) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[(mb * 16 + r) * 64 + lane] = dqacc[mb][r];
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((db * 2 + qb) * 4 + i) * 64 + lane] = dqacc[db][qb][i];
     }
     __syncthreads();
     if (grp == 1) return;
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dqacc[mb][r] += red[(mb * 16 + r) * 64 + lane];
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dqacc[db][qb][i] += red[((db * 2 + qb) * 4 + i) * 64 + lane];
   }
 
-  if (qrow < nq) {
-    const long off = ((long)sl.qrow0 + qrow) * rs + (long)sl.qhead * D + 4 * hl;
+  // lane (c, g) stores d = 16 db + 4g .. +3 of its two rows
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw + 16 * qb + c;
+    if (qrow < nq) {
+      const long off = ((long)sl.qrow0 + qrow) * rs + (long)sl.qhead * D + 4 * g;
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const long o = off + 32 * mb + 8 * j4;
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = dqacc[mb][4 * j4 + e] * p.scale;
+      for (int db = 0; db < ND; ++db) {
+        const long o = off + 16 * db;
+        const f32x4 x = dqacc[db][qb] * p.scale;
         if (ACC) {
           f32x4* a = reinterpret_cast<f32x4*>(p.dq_acc + o);
-          if (p.acc_flags & 1) x += *a;
-          *a = x;
+          *a = (p.acc_flags & 1) ? *a + x : x;
         } else {
           *reinterpret_cast<bf16x4*>(p.dq + o) = to_bf16x4(x);
         }
       }
+    }
   }
 }
 

@@ -19,15 +19,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "attention_flash_attn_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Spill bytes per lane allowed per kernel instance (demangled name).  The D = 128 backward
-# holds 16 registers of the row's -delta through its dQ key loop; the dense instance then
-# stores three registers before that loop and reloads them after it, the varlen instance
-# (sequence bounds, longest-first order) six, one of them reloaded in the loop.  The dense
-# D = 128 forward (two queries per lane on 16x16x32 products) stores two registers before
-# its key loops and reloads them after.  Every other kernel must not spill at all.
+# Spill bytes per lane allowed per kernel instance (demangled name).  The dense D = 128
+# backward (plain and accumulating) stores four registers before its dQ key loop (two
+# queries per lane on 16x16x32 products, Q and dO of both held) and reloads two of them
+# once per key tile.  The dense D = 128 forward stores two registers before its key loops
+# and reloads them after.  Every other kernel must not spill at all.
 MAX_SCRATCH = {
-    "attn::bwd_kernel<128, false, false>": 16,
-    "attn::bwd_kernel<128, true, false>": 24,
+    "attn::bwd_kernel<128, false, false>": 20,
+    "attn::bwd_kernel<128, false, true>": 20,
     "attn::fwd_kernel<128, false>": 12,
 }
 
