@@ -14,19 +14,25 @@
 // dK/dV and dQ come from two kernels that each own their output rows, so
 // there are no atomics and the result is bitwise reproducible.
 //
+// Both workgroup kinds run their products on v_mfma_f32_16x16x32_bf16, which delivers
+// more FLOP/s than the 32x32x16 shape under the package power limit (half the accumulator
+// traffic per multiply-add); every LDS fragment read feeds two or four MFMAs, so the LDS
+// bytes per FLOP are those of the 32x32x16 layout.
+//
 // dK/dV workgroup: 8 waves, 256 keys.  The keys' K rows go to registers and their V rows
 // sit in LDS for the whole loop; query tiles of 64 rows (Q, dO, LSE, delta) are
 // double-buffered in LDS, filled asynchronously by buffer loads into XOR-swizzled LDS
-// rows (tile.hpp).  Wave w owns key block w (32 keys, one per lane of the score tile
-// S = Q K^T) and both 32-row halves of every tile, with its dK^T, dV^T accumulators in
-// registers across the loop.  Q^T and dO^T operands come from the LDS transposing read.
+// rows (tile.hpp; natural row order).  Wave w owns keys 32w .. 32w+31
+// (two 16-key blocks: two keys per lane, the columns of the score blocks S = Q K^T) and
+// both 32-row halves of every tile, with its dK^T, dV^T accumulators in registers across
+// the loop.  Q^T and dO^T operands come from the LDS transposing read, in the row order of
+// the lane's P and dS values.
 //
-// dQ workgroup: 8 waves, 256 query rows, products on v_mfma_f32_16x16x32_bf16 (more
-// FLOP/s than 32x32x16 under the power limit); each wave keeps its 32 rows of Q and dO
-// (B operands of S^T = K Q^T and dP^T = V dO^T in two 16-query blocks: two queries per
-// lane, so LSE and delta are per-lane scalars) and its dQ^T accumulator in registers; K/V
-// tiles of 64 keys are double-buffered in LDS the same way (the 16x16 swizzle, natural row
-// order); K^T comes from the transposing read, in the key order of the lane's dS values.
+// dQ workgroup: 8 waves, 256 query rows; each wave keeps its 32 rows of Q and dO (B
+// operands of S^T = K Q^T and dP^T = V dO^T in two 16-query blocks: two queries per lane,
+// so LSE and delta are per-lane scalars) and its dQ^T accumulator in registers; K/V tiles
+// of 64 keys are double-buffered in LDS the same way; K^T comes from the transposing read,
+// in the key order of the lane's dS values.
 //
 // Eight waves, two per SIMD, keep each wave within 256 registers, so that one wave's
 // matrix instructions run while the other does its exponentials and conversions (a wave
@@ -118,22 +124,6 @@ __device__ __forceinline__ Slice decode(const BwdParams& p, int group, int tile,
   return s;
 }
 
-// The 16 per-row values of a score register tile, from LDS: register r's row value sits at
-// p[16 * (r / 8) + r % 8].
-__device__ __forceinline__ f32x16 row_values16(const float* p) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-  const f32x4 c = *reinterpret_cast<const f32x4*>(p + 16), d = *reinterpret_cast<const f32x4*>(p + 20);
-  f32x16 v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = a[i];
-    v[4 + i] = b[i];
-    v[8 + i] = c[i];
-    v[12 + i] = d[i];
-  }
-  return v;
-}
-
 // ------------------------------------------------------------------ dK / dV
 
 template <int D>
@@ -157,37 +147,25 @@ struct DqSmem {
   char v[2][BN * 2 * D];
 };
 
-// Per-lane offsets of the transposing reads of a kRowPerm-ordered 32-row block: for
-// lane group g and source lane src, reduction half `half` of MFMA step t covers tile
-// rows 16t + 8*(g/2) + 4*half + src/4, stored at LDS row 16t + 8*half + 4*(g/2) + src/4.
-template <int D>
-__device__ __forceinline__ void perm_tr_offsets(int lane, int (&off)[D / 32][2]) {
-  const int g = lane >> 4, src = lane & 15;
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-      off[mb][half] = tile_off_tr<D>(8 * half + 4 * (g >> 1) + (src >> 2),
-                                     32 * mb + 16 * (g & 1) + 4 * (src & 3));
-}
-
-// dK/dV: 8 waves, 256 keys.  Wave w owns key block w (32 keys, one per lane) and both
-// 32-row halves of every 64-row query tile, so each staged tile feeds 64 MFMAs per wave
-// and no two waves share a key.  The wave's K fragments (the B operand of S = Q K^T, 32
-// registers) are read from LDS once and kept in registers for the whole loop; V stays in
-// LDS, which keeps a wave within 256 registers: two waves per SIMD, so one wave's MFMAs
-// run while the other does its softmax VALU work.
+// dK/dV: 8 waves, 256 keys.  Wave w owns keys 32w .. 32w+31 and both 32-row halves of
+// every 64-row query tile, so each staged tile feeds 128 MFMAs per wave and no two waves
+// share a key.  The wave's K fragments (the B operands of S = Q K^T, 32 registers) are read
+// from LDS once and kept in registers for the whole loop; V stays in LDS, which keeps a
+// wave within 256 registers: two waves per SIMD, so one wave's MFMAs run while the other
+// does its softmax VALU work.
 template <int D, bool VARLEN, bool ACC>
 __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, DkdvSmem<D>& sm) {
   constexpr int BN = DkdvSmem<D>::BN, BQ = DkdvSmem<D>::BQ, NW = 8;
   constexpr int RB = 2 * D;
-  constexpr int NKS = D / 16, NMB = D / 32;
+  constexpr int NKS = D / 32, ND = D / 16;
   static_assert(sizeof(sm.q) + sizeof(sm.o) == BN * RB && offsetof(DkdvSmem<D>, q) == 0,
                 "the Q/dO buffers stage K");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-  const int hl = lane >> 5, l32 = lane & 31;
+  // 16x16x32 operand roles: lane = 16 g + c holds column / row c of a block and reduction
+  // slots 8g .. 8g+7; an output block gives it column c, rows 4g .. 4g+3.
+  const int g = lane >> 4, c = lane & 15;
   const int kb0 = sl.tile * BN;
   if (kb0 >= sl.nk) return;  // block-uniform
   // Q/dO rows hold H heads, K/V/dK/dV rows Hk.  The loop runs over the query tiles of all
@@ -196,55 +174,61 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   const long rs = (long)p.H * D, rsk = (long)p.Hk * D;
   const int nq = sl.nq, nk = sl.nk;
 
-  const int key = kb0 + 32 * wave + l32;
-  bool kvalid = key < nk;
-  if (kvalid && sl.mask) kvalid = sl.mask[key] != 0;
-  const uint64_t kball = __ballot(kvalid);
-  if (!__syncthreads_or(kvalid)) {
+  // The wave's 32 keys in two 16-key blocks; the lane's keys are kw + c and kw + 16 + c.
+  const int kw = kb0 + 32 * wave;
+  bool kvalid[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw + 16 * kb + c;
+    kvalid[kb] = key < nk && (!sl.mask || sl.mask[key] != 0);
+  }
+  const uint64_t kball = __ballot(kvalid[0] || kvalid[1]);
+  if (!__syncthreads_or(kvalid[0] || kvalid[1])) {
     // Every key of the workgroup is masked: dK = dV = 0 without the query loop (added to
     // nothing when accumulating).
-    if (key < nk && !(ACC && (p.acc_flags & 2))) {
-      const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * hl;
+    if (!(ACC && (p.acc_flags & 2))) {
 #pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const long o = off + 8 * c;
-        if (ACC) {
-          *reinterpret_cast<f32x4*>(p.dk_acc + o) = f32x4{};
-          *reinterpret_cast<f32x4*>(p.dv_acc + o) = f32x4{};
-        } else {
-          *reinterpret_cast<bf16x4*>(p.dk + o) = to_bf16x4(f32x4{});
-          *reinterpret_cast<bf16x4*>(p.dv + o) = to_bf16x4(f32x4{});
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw + 16 * kb + c;
+        if (key >= nk) continue;
+        const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const long o = off + 16 * db;
+          if (ACC) {
+            *reinterpret_cast<f32x4*>(p.dk_acc + o) = f32x4{};
+            *reinterpret_cast<f32x4*>(p.dv_acc + o) = f32x4{};
+          } else {
+            *reinterpret_cast<bf16x4*>(p.dk + o) = to_bf16x4(f32x4{});
+            *reinterpret_cast<bf16x4*>(p.dv + o) = to_bf16x4(f32x4{});
+          }
         }
       }
     }
     return;
   }
 
-  // LDS offsets.  Row reads of reduction step ks differ only in chunk bits, offset(ks) =
-  // offset(0) ^ 32 ks, and the transposing reads of column block mb likewise, offset(mb) =
-  // offset(0) ^ 64 mb (tile.hpp swizzle).  They are rebuilt before every use from the
-  // step-0 offsets (3 registers instead of 16 held through the loop).
-  int qoff0 = tile_off<D>(l32, hl), tr0[2];
-  {
-    int t[NMB][2];
-    perm_tr_offsets<D>(lane, t);
-    tr0[0] = t[0][0];
-    tr0[1] = t[0][1];
-  }
-  int qoff[NKS], troff[NMB][2];
+  // LDS offsets.  Q/dO/K/V fragment of 16-row block rb, step ks: row 16 rb + c, chunk
+  // 4 ks + g; Q^T/dO^T fragment of d block db in a 32-row step: rows 4g + e and 16 + 4g + e
+  // at d = 16 db + c (transposing reads).  Steps differ only in chunk bits, offset(ks) =
+  // offset(0) ^ 64 ks and offset(db) = offset(0) ^ 32 db (tile.hpp swizzle); they are
+  // rebuilt before every use from the step-0 offsets (3 registers held through the loop).
+  int qoff0 = tile_off<D>(c, g), tr0[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) tr0[h] = tile_off_tr<D>(16 * h + 4 * g + (c >> 2), 4 * (c & 3));
+  int qoff[NKS], troff[ND][2];
   auto offsets = [&]() {
     asm volatile("" : "+v"(qoff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qoff[ks] = qoff0 ^ (32 * ks);
+    for (int ks = 0; ks < NKS; ++ks) qoff[ks] = qoff0 ^ (64 * ks);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      troff[mb][0] = tr0[0] ^ (64 * mb);
-      troff[mb][1] = tr0[1] ^ (64 * mb);
+    for (int db = 0; db < ND; ++db) {
+      troff[db][0] = tr0[0] ^ (32 * db);
+      troff[db][1] = tr0[1] ^ (32 * db);
     }
   };
 
   auto same_row = [](int r) { return r; };
-  auto qrow_of = [](int r) { return perm32_row(r); };
   const bf16* kbase = p.k + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   const bf16* qbase = p.q + (long)sl.qrow0 * rs + (long)sl.qhead * D;
@@ -257,7 +241,7 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     kvld.issue(sm.v, vbase, rsk, kb0, nk);
   }
   TileLoader<D, BQ, 4> ld;  // used by waves 0..3
-  ld.init(rs, qrow_of);
+  ld.init(rs, same_row);
   // LSE and delta of the next tile are loaded raw (row clamped, no arithmetic) ahead of
   // its asynchronous copy and only used when published after the current tile's
   // compute: a use right after the load would make the wave wait for the whole copy.
@@ -299,61 +283,88 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     }
   };
 
-  f32x16 dkacc[NMB], dvacc[NMB];
+  f32x4 dkacc[ND][2], dvacc[ND][2];  // dK^T / dV^T block (d 16 db + 4g + i, key 16 kb + c)
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) dkacc[mb] = dvacc[mb] = f32x16{};
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dkacc[db][kb] = dvacc[db][kb] = f32x4{};
   const float c2 = p.c2;
   const int kr = wave * 32 * RB;
-  bf16x8 kreg[NKS];  // this wave's 32 keys as the B operand of S = Q K^T, one per ks
+  bf16x8 kreg[2][NKS];  // the wave's keys as the B operand of S = Q K^T: key 16 kb + c, d 32 ks + 8g ..
 
-  // dP = dO V^T of both 32-row halves of a tile (one key per lane), so that each V fragment
-  // read feeds two MFMAs.  The accumulators start from their rows' -delta.
-  auto scores_dp = [&](const char* vt, const char* ot, const float* dt, f32x16& dp0, f32x16& dp1) {
+  // dP = dO V^T of the whole 64-row tile (query block qb = 0..3, key block kb), so that
+  // each V fragment read feeds four MFMAs.  The accumulators start from their rows' -delta.
+  auto scores_dp = [&](const char* vt, const char* ot, const float* dt, f32x4 (&dp)[4][2]) {
     offsets();
-    dp0 = row_values16(dt + 8 * hl);
-    dp1 = row_values16(dt + 32 + 8 * hl);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 vf = lds_row16(vt, kr + qoff[ks]);
-      dp0 = mfma32(lds_row16(ot, qoff[ks]), vf, dp0);
-      dp1 = mfma32(lds_row16(ot, 32 * RB + qoff[ks]), vf, dp1);
-    }
-  };
-  // One 32x32 (query x key) step on half u of the tile, given its dP: scores S = Q K^T (one
-  // key per lane), weights P = exp(scale S - LSE) and dS = P (dP - delta), then
-  // dV^T += dO^T P and dK^T += Q^T dS.  The S and dP accumulators start from their rows'
-  // -LSE/scale and -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in
-  // registers.  No key-mask work here: with one key per lane, P and dS of an excluded key
-  // only reach that key's own accumulators, which are stored as zeros.  Causal blocks that
-  // hold a key after one of their rows zero P per element in a branch taken only there.
-  auto compute = [&](const char* qt, const char* ot, const float* lt, int q0, int u, f32x16 dp) {
-    const int qr = u * 32 * RB;
-    offsets();
-    // Register r holds query 32*u + 16*(r/8) + 8*hl + r%8 of the tile.
-    f32x16 s = row_values16(lt + 32 * u + 8 * hl);
+    for (int qb = 0; qb < 4; ++qb) dp[qb][0] = dp[qb][1] = *reinterpret_cast<const f32x4*>(dt + 16 * qb + 4 * g);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      s = mfma32(lds_row16(qt, qr + qoff[ks]), kreg[ks], s);
-    if (p.causal && q0 + 32 * u < kb0 + 32 * wave + 31) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 vf = lds_row16(vt, kr + 16 * kb * RB + qoff[ks]);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) dp[qb][kb] = mfma16(lds_row16(ot, 16 * qb * RB + qoff[ks]), vf, dp[qb][kb]);
+      }
+  };
+  // One 32x32 (query x key) step on half u of the tile (query blocks 2u, 2u + 1), given its
+  // dP: scores S = Q K^T, weights P = exp(scale S - LSE) and dS = P (dP - delta), then
+  // dV^T += dO^T P and dK^T += Q^T dS.  The S and dP accumulators start from their rows'
+  // -LSE/scale and -delta, so P = exp2(c2 acc) and dS = P acc with no per-row operands in
+  // registers.  No key-mask work here: P and dS of an excluded key only reach that key's
+  // own accumulators (keys are output columns), which are stored as zeros.  Causal blocks
+  // that hold a key after one of their rows zero P per element in a branch taken only there.
+  auto compute = [&](const char* qt, const char* ot, const float* lt, int q0, int u, f32x4 (&dp)[4][2]) {
+    const int qr = u * 32 * RB;
+    offsets();
+    // s[b][kb]: query 32u + 16b + 4g + i of the tile, key 16 kb + c of the wave
+    f32x4 s[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) s[b][0] = s[b][1] = *reinterpret_cast<const f32x4*>(lt + 32 * u + 16 * b + 4 * g);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bf16x8 a = lds_row16(qt, qr + 16 * b * RB + qoff[ks]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[b][kb] = mfma16(a, kreg[kb][ks], s[b][kb]);
+      }
+    if (p.causal && q0 + 32 * u < kw + 31) {
       keep_branch();
-      // P = 0 where this lane's key comes after register r's row.
-      const int first = key - q0 - 32 * u - 8 * hl;  // row offset below which P = 0
+      // P = 0 where the lane's key comes after the value's row.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 16 * (r >> 3) + (r & 7) >= first ? s[r] : -INFINITY;
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[b][kb][i] = kw + 16 * kb + c <= q0 + 32 * u + 16 * b + 4 * g + i ? s[b][kb][i] : -INFINITY;
+    }
+    // pk[kb], ds[kb]: the B operands of the dV^T / dK^T steps (rows 4g + i of block 2u,
+    // then of block 2u + 1)
+    bf16x8 pk[2], ds[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 x, y;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pw = __builtin_amdgcn_exp2f(s[b][kb][i] * c2);
+          x[4 * b + i] = pw;
+          y[4 * b + i] = pw * dp[2 * u + b][kb][i];
+        }
+      pk[kb] = pack8(x, 0);
+      ds[kb] = pack8(y, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(s[r] * c2);
-      dp[r] = s[r] * dp[r];
-    }
-    const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
-    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
+    for (int db = 0; db < ND; ++db) {
+      const bf16x8 ao = lds_tr8(ot + qr, troff[db][0], troff[db][1]);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      dvacc[mb] = mfma32(lds_tr8(ot + qr, troff[mb][0], troff[mb][1]), pk0, dvacc[mb]);
-      dvacc[mb] = mfma32(lds_tr8(ot + qr + 16 * RB, troff[mb][0], troff[mb][1]), pk1, dvacc[mb]);
-      dkacc[mb] = mfma32(lds_tr8(qt + qr, troff[mb][0], troff[mb][1]), ds0, dkacc[mb]);
-      dkacc[mb] = mfma32(lds_tr8(qt + qr + 16 * RB, troff[mb][0], troff[mb][1]), ds1, dkacc[mb]);
+      for (int kb = 0; kb < 2; ++kb) dvacc[db][kb] = mfma16(ao, pk[kb], dvacc[db][kb]);
+      const bf16x8 aq = lds_tr8(qt + qr, troff[db][0], troff[db][1]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dkacc[db][kb] = mfma16(aq, ds[kb], dkacc[db][kb]);
     }
   };
 
@@ -369,15 +380,15 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
     if (more) issue(j + 1, nq_, no_);
     if (kball != 0) {
       const int q0 = tile_q0(j);
-      f32x16 dp0, dp1;
-      scores_dp(vt, co, cd, dp0, dp1);
-      compute(cq, co, cl, q0, 0, dp0);
+      f32x4 dp[4][2];
+      scores_dp(vt, co, cd, dp);
+      compute(cq, co, cl, q0, 0, dp);
       // The two waves of a SIMD do the same work, but waves 0..3 start late (copy issue)
       // and then win every tie (older waves issue first), so they finish early and wait at
       // the barrier while their partner runs alone.  Waves 4..7 take priority for their
       // second half, so both finish about together.
       if (wave >= 4) __builtin_amdgcn_s_setprio(1);
-      compute(cq, co, cl, q0, 1, dp1);
+      compute(cq, co, cl, q0, 1, dp);
       if (wave >= 4) __builtin_amdgcn_s_setprio(0);
     }
     if (more) publish_stats(j + 1, nl, nd);
@@ -390,7 +401,9 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   __syncthreads();
   offsets();
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) kreg[ks] = lds_row16(kstage, kr + qoff[ks]);
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kreg[kb][ks] = lds_row16(kstage, kr + 16 * kb * RB + qoff[ks]);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();
   if (ntiles > 0) {
@@ -405,34 +418,31 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
       step(j + 1, sm.v, sm.q[1], sm.o[1], sm.l[1], sm.d[1], sm.q[0], sm.o[0], sm.l[0], sm.d[0]);
   }
 
-  if (key < nk) {
-    const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * hl;
+  // lane (c, g) stores d = 16 db + 4g .. +3 of its two keys
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw + 16 * kb + c;
+    if (key >= nk) continue;
+    const long off = ((long)sl.krow0 + key) * rsk + (long)sl.kvhead * D + 4 * g;
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        f32x4 a, b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j4 + e;
-          a[e] = kvalid ? dkacc[mb][r] * p.scale : 0.f;
-          b[e] = kvalid ? dvacc[mb][r] : 0.f;
+    for (int db = 0; db < ND; ++db) {
+      f32x4 a = kvalid[kb] ? dkacc[db][kb] * p.scale : f32x4{};
+      f32x4 b = kvalid[kb] ? dvacc[db][kb] : f32x4{};
+      const long o = off + 16 * db;
+      if (ACC) {
+        f32x4* ka = reinterpret_cast<f32x4*>(p.dk_acc + o);
+        f32x4* va = reinterpret_cast<f32x4*>(p.dv_acc + o);
+        if (p.acc_flags & 2) {
+          a += *ka;
+          b += *va;
         }
-        const long o = off + 32 * mb + 8 * j4;
-        if (ACC) {
-          f32x4* ka = reinterpret_cast<f32x4*>(p.dk_acc + o);
-          f32x4* va = reinterpret_cast<f32x4*>(p.dv_acc + o);
-          if (p.acc_flags & 2) {
-            a += *ka;
-            b += *va;
-          }
-          *ka = a;
-          *va = b;
-        } else {
-          *reinterpret_cast<bf16x4*>(p.dk + o) = to_bf16x4(a);
-          *reinterpret_cast<bf16x4*>(p.dv + o) = to_bf16x4(b);
-        }
+        *ka = a;
+        *va = b;
+      } else {
+        *reinterpret_cast<bf16x4*>(p.dk + o) = to_bf16x4(a);
+        *reinterpret_cast<bf16x4*>(p.dv + o) = to_bf16x4(b);
       }
+    }
   }
 }
 
@@ -496,9 +506,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   // the step-0 offsets (3 registers held through the loop).  The offsets also carry the wave
   // group's distance to its own tiles (GB, a multiple of 256 bytes, which the XORs leave
   // alone), so the tile addresses stay constants.
-  int koff0 = tile_off<D, true>(c, g) + grp * GB, tr0[2];
+  int koff0 = tile_off<D>(c, g) + grp * GB, tr0[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) tr0[h] = tile_off_tr<D, true>(16 * h + 4 * g + (c >> 2), 4 * (c & 3)) + grp * GB;
+  for (int h = 0; h < 2; ++h) tr0[h] = tile_off_tr<D>(16 * h + 4 * g + (c >> 2), 4 * (c & 3)) + grp * GB;
   int koff[NKS], troff[ND][2];
   auto offsets = [&]() {
     asm volatile("" : "+v"(koff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
@@ -514,7 +524,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   const bf16* kbase = p.k + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   const bf16* vbase = p.v + (long)sl.krow0 * rsk + (long)sl.kvhead * D;
   auto same_row = [](int r) { return r; };
-  TileLoader<D, BN, 4, true> ld;  // used by waves 0..3 (split: each group's four waves)
+  TileLoader<D, BN, 4> ld;  // used by waves 0..3 (split: each group's four waves)
   ld.init(rsk, same_row, 4 * grp);
   // Only waves 0..3 copy (see dkdv_block): while they stall at issue, waves 4..7, one per
   // SIMD, keep the matrix units busy.  In a split workgroup each group copies its own tiles.

@@ -1,13 +1,13 @@
 // common.hpp -- device helpers shared by the libattn kernels (gfx950 only).
 //
-// MFMA operand layouts of v_mfma_f32_32x32x16_bf16 (wave64; the backward's products):
-//   A (32 x 16):  lane l holds row l%32, reduction slots 8*(l/32) .. +7
-//   B (16 x 32):  lane l holds column l%32, reduction slots 8*(l/32) .. +7
-//   C (32 x 32):  lane l holds column l%32; register r holds row
-//                 8*(r/4) + 4*(l/32) + r%4
-// Any fixed assignment of reduction slots to a real index works as long as A
-// and B agree, which is how score tiles are fed back in as operands without a
-// shuffle (see kRowPerm).
+// MFMA: every product runs on v_mfma_f32_16x16x32_bf16 (wave64; layout verified on the
+// GPU with an in-bounds probe):
+//   A (16 x 32): lane l holds row l%16, reduction slots 8*(l/16) .. +7
+//   B (32 x 16): lane l holds column l%16, reduction slots 8*(l/16) .. +7
+//   C (16 x 16): lane l holds column l%16; register i holds row 4*(l/16) + i
+// Any fixed assignment of reduction slots to a real index works as long as A and B agree,
+// which is how score blocks are fed back in as operands without a shuffle: the kernels'
+// transposing reads fetch the other operand in the order the score registers hold.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,30 +34,9 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// v_mfma_f32_16x16x32_bf16 (verified on the GPU with an in-bounds probe):
-//   A (16 x 32): lane l holds row l%16, reduction slots 8*(l/16) .. +7
-//   B (32 x 16): lane l holds column l%16, reduction slots 8*(l/16) .. +7
-//   C (16 x 16): lane l holds column l%16; register i holds row 4*(l/16) + i
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// Row permutation inside a 32-row block: swaps bit 2 and bit 3 of the index.
-// If LDS row p of a tile holds tile row kRowPerm(p), then a 32x32 MFMA result
-// whose rows come from LDS rows 0..31 has, in lane half h, registers
-// r = 8t + s (t in {0,1}, s in 0..7) holding tile row 16t + 8h + s: eight
-// consecutive rows per register octet, exactly the B-operand slot order of the
-// next MFMA step.  The permutation is an involution.
-__device__ __forceinline__ int kRowPerm(int p) {
-  return (p & 0x13) | ((p & 0x8) >> 1) | ((p & 0x4) << 1);
-}
-
-// Register r of a 32x32 C tile in lane half h holds (after kRowPerm) tile row:
-__device__ __forceinline__ int c_row_permuted(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
 // 16-byte global load / store as raw bits.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -106,18 +85,5 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // side effects, so the compiler keeps the branch instead of flattening its body
 // into selects executed on every iteration.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
-
-// Reductions over lane pairs (l, l^32), i.e. the two halves of a wave, with
-// v_permlane32_swap on two copies of x: the swapped pair holds x[l%32] and
-// x[l%32 + 32] in every lane l.
-__device__ __forceinline__ float wave_max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return a > b ? a : b;
-}
-__device__ __forceinline__ float wave_sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 }  // namespace attn

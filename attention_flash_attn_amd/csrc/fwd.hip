@@ -15,7 +15,7 @@
 //    per-lane partials, combined across the four lanes only where needed.
 //  * K/V tiles of 64 keys are double- or triple-buffered in LDS and filled
 //    asynchronously by buffer loads into LDS.  Tiles are unpadded and XOR-swizzled
-//    (tile.hpp, the 16x16 swizzle) so the row reads of K and the transposing reads of V
+//    (tile.hpp) so the row reads of K and the transposing reads of V
 //    are bank-conflict free.  The score registers of a lane (keys 4g..4g+3 and 16+4g..
 //    16+4g+3 of each 32-key step, g = lane / 16) are directly the B operand of
 //    O^T += V^T P^T; the transposing reads of V fetch the same key order.
@@ -142,14 +142,14 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // addresses row 4g + e (+16), columns 16 db + 4t .. +3).
   int koff[NKS], voff[ND][2];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D, true>(c, 4 * ks + g);
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = tile_off<D>(c, 4 * ks + g);
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      voff[db][h] = tile_off_tr<D, true>(16 * h + 4 * g + (c >> 2), 16 * db + 4 * (c & 3));
+      voff[db][h] = tile_off_tr<D>(16 * h + 4 * g + (c >> 2), 16 * db + 4 * (c & 3));
 
-  TileLoader<D, BN, 4, true> kld, vld;  // the masked / causal loop: used by group B only
+  TileLoader<D, BN, 4> kld, vld;  // the masked / causal loop: used by group B only
   auto same_row = [](int r) { return r; };
   kld.init(rsk, same_row, 4);
   vld.init(rsk, same_row, 4);
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     char* const dV2 = smem + 5 * TILE;
     // One loader per wave: group A copies K, group B copies V.  (Choosing between two loader
     // objects per group would put them in scratch memory.)
-    TileLoader<D, BN, 4, true> cld;
+    TileLoader<D, BN, 4> cld;
     cld.init(rsk, same_row, 4 * grp_b);
     const bf16* const cbase = grp_b ? vbase : kbase;
     const int lead = grp_b ? 1 : 2;  // group A copies K(j+2), group B V(j+1)
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     const int nts = (kend + BNS - 1) / BNS;
     const int hn = (nts + S - 1) / S, t0 = grp * hn, t1 = min(nts, t0 + hn);
     char* const gb = smem + 4 * TS * grp;
-    TileLoader<D, BNS, RBK, true> gk, gv;
+    TileLoader<D, BNS, RBK> gk, gv;
     gk.init(rsk, same_row, RBK * grp);
     gv.init(rsk, same_row, RBK * grp);
     auto word = [&](int j, uint32_t bytes) -> uint64_t __attribute__((always_inline)) {

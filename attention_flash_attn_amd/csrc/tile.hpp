@@ -3,14 +3,14 @@
 //
 // A tile holds R rows of D bf16 (2*D bytes per row, no padding).  The 16-byte
 // chunk c of row r is stored at chunk position c ^ swz(r).  The swizzle makes the
-// two read patterns the kernels use conflict-free on the 64 x 4-byte LDS banks:
+// two read patterns of the 16x16x32 operands conflict-free on the 64 x 4-byte LDS banks:
 //  * row-wise 16-byte reads (MFMA operand rows): 16 lanes read 16 consecutive rows
-//    at the same logical chunk -> 16 distinct bank groups;
-//  * transposing 8-byte reads (ds_read_b64_tr_b16): in the backward's 32x32x16
-//    operands 32 lanes read 4 consecutive rows (aligned to 4) x 4 consecutive chunks
-//    (aligned to 4); in the forward's 16x16x32 operands they read 8 consecutive rows
-//    (aligned to 8) x 2 adjacent chunks.  Each pattern has its own swizzle (swz<D, S16>),
-//    and both give 16 distinct 16-byte bank groups.
+//    at the same logical chunk -> 16 distinct bank groups (swz is a bijection on r & 15;
+//    at D = 64, where two rows share 256 bytes of banks, on the rows of one parity);
+//  * transposing 8-byte reads (ds_read_b64_tr_b16): each 32-lane half reads 8
+//    consecutive rows (aligned to 8) x 2 adjacent chunks {2m, 2m+1}, so swz(r) >> 1 must
+//    differ among those rows (D = 64: among the 4 rows of one parity) -> 16 distinct
+//    16-byte bank groups.
 // swz depends only on r & 15, so moving by a multiple of 16 rows keeps offsets.
 //
 // buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at M0 + 16*l, i.e. one
@@ -26,29 +26,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Word 3 of a raw buffer resource (stride 0, byte-addressed, 32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
 
-// Two swizzles.  The first (S16 = false, the backward's tiles) serves transposing reads of
-// 4 rows x 4 chunks per 16 lanes (32x32x16 operands).  The second (S16 = true, the forward's
-// tiles) serves the 16x16x32 operands: transposing reads in which each 32-lane half reads 8
-// consecutive rows (aligned to 8) x 2 adjacent chunks {2m, 2m+1}, i.e. swz(r) >> 1 must differ
-// among those rows (D = 128: over the 8 rows; D = 64, two rows per 256 bytes of banks: over
-// the 4 rows of one parity).  Both keep 16-lane row reads of 16 consecutive rows conflict-free.
-template <int D, bool S16 = false>
+template <int D>
 __device__ __forceinline__ int swz(int r) {
   static_assert(D == 64 || D == 128, "head dim");
-  if (S16) return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-  return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
 }
 
 // Byte offset of (row r, logical 16-byte chunk c) inside a tile.
-template <int D, bool S16 = false>
+template <int D>
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return r * (2 * D) + ((c ^ swz<D, S16>(r)) << 4);
+  return r * (2 * D) + ((c ^ swz<D>(r)) << 4);
 }
 
 // Byte offset of the 8-byte group holding elements [col, col+4) of row r (col % 4 == 0).
-template <int D, bool S16 = false>
+template <int D>
 __device__ __forceinline__ int tile_off_tr(int r, int col) {
-  return tile_off<D, S16>(r, col >> 3) + 2 * (col & 7);
+  return tile_off<D>(r, col >> 3) + 2 * (col & 7);
 }
 
 __device__ __forceinline__ bf16x8 lds_row16(const char* tile, int byte_off) {
@@ -68,11 +61,12 @@ __device__ __forceinline__ bf16x8 lds_tr8(const char* tile, int off_lo, int off_
 // keeps only 32-bit offsets.  Lane-dependent parts of the offsets are fixed per kernel,
 // so they are computed once: off[i] is the byte offset, from the tile's first row, of the
 // 16-byte chunk this lane fetches with its i-th instruction.  row_of(r) maps tile row r
-// to its row offset within the tile (a permutation of 0..ROWS-1).  In a tile that runs
+// to its row offset within the tile (a permutation of 0..ROWS-1; the kernels use the
+// identity).  In a tile that runs
 // past the last valid row, the copies of the missing rows fall outside the buffer range
 // and fill their LDS with zeros (issue() below): every access stays inside the tensor, and
 // a tail tile costs no per-lane work.
-template <int D, int ROWS, int NW, bool S16 = false>
+template <int D, int ROWS, int NW>
 struct TileLoader {
   static constexpr int CPR = D / 8;            // chunks per row
   static constexpr int RPI = 1024 / (2 * D);   // rows per instruction (4 or 8)
@@ -89,7 +83,7 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = (wave + i * NW) * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D, S16>(r);
+      const int c = (lane % CPR) ^ swz<D>(r);
       off[i] = (uint32_t)(2 * ((long)row_of(r) * rs + 8 * c));
     }
   }
@@ -111,8 +105,6 @@ struct TileLoader {
     for (int i = 0; i < NI; ++i) load(r, tile, i, off[i]);
   }
 };
-
-__device__ __forceinline__ int perm32_row(int r) { return (r & ~31) | kRowPerm(r & 31); }
 
 // Key validity of the tiles of a loop over keys: bit i of a tile's word says that key
 // k0 + i exists and is not excluded by the mask.  The mask bytes are read raw (index
