@@ -299,13 +299,17 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) dp[qb][0] = dp[qb][1] = *reinterpret_cast<const f32x4*>(dt + 16 * qb + 4 * g);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {  // each V and dO fragment read once per step
+      bf16x8 vf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 vf = lds_row16(vt, kr + 16 * kb * RB + qoff[ks]);
+      for (int kb = 0; kb < 2; ++kb) vf[kb] = lds_row16(vt, kr + 16 * kb * RB + qoff[ks]);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) dp[qb][kb] = mfma16(lds_row16(ot, 16 * qb * RB + qoff[ks]), vf, dp[qb][kb]);
+      for (int qb = 0; qb < 4; ++qb) {
+        const bf16x8 a = lds_row16(ot, 16 * qb * RB + qoff[ks]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dp[qb][kb] = mfma16(a, vf[kb], dp[qb][kb]);
       }
+    }
   };
   // One 32x32 (query x key) step on half u of the tile (query blocks 2u, 2u + 1), given its
   // dP: scores S = Q K^T, weights P = exp(scale S - LSE) and dS = P (dP - delta), then
@@ -329,6 +333,17 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s[b][kb] = mfma16(a, kreg[kb][ks], s[b][kb]);
       }
+    {
+      // one Q fragment read per two MFMAs, issued AHEAD fragments early (measured: 1.6% on
+      // the backward together with the read-ahead below; more or less ahead was slower)
+      constexpr int AHEAD = 4, R = 2 * NKS;
+      ATTN_SCHED(kSchedDSRead, AHEAD);
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        ATTN_SCHED(kSchedMFMA, 2);
+        if (n + AHEAD < R) ATTN_SCHED(kSchedDSRead, 1);
+      }
+    }
     if (p.causal && q0 + 32 * u < kw + 31) {
       keep_branch();
       // P = 0 where the lane's key comes after the value's row.
@@ -365,6 +380,15 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
       const bf16x8 aq = lds_tr8(qt + qr, troff[db][0], troff[db][1]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) dkacc[db][kb] = mfma16(aq, ds[kb], dkacc[db][kb]);
+    }
+    {
+      constexpr int AHEAD = 3, F = 2 * ND;  // fragments of two transposing reads, two MFMAs each
+      ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
+#pragma unroll
+      for (int n = 0; n < F; ++n) {
+        ATTN_SCHED(kSchedMFMA, 2);
+        if (n + AHEAD < F) ATTN_SCHED(kSchedDSRead, 2);
+      }
     }
   };
 
