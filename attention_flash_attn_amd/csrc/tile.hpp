@@ -2,16 +2,30 @@
 // asynchronously by buffer_load_dwordx4 ... lds.
 //
 // A tile holds R rows of D bf16 (2*D bytes per row, no padding).  The 16-byte
-// chunk c of row r is stored at chunk position c ^ swz(r).  The swizzle makes the
-// two read patterns of the 16x16x32 operands conflict-free on the 64 x 4-byte LDS banks:
-//  * row-wise 16-byte reads (MFMA operand rows): 16 lanes read 16 consecutive rows
-//    at the same logical chunk -> 16 distinct bank groups (swz is a bijection on r & 15;
-//    at D = 64, where two rows share 256 bytes of banks, on the rows of one parity);
-//  * transposing 8-byte reads (ds_read_b64_tr_b16): each 32-lane half reads 8
-//    consecutive rows (aligned to 8) x 2 adjacent chunks {2m, 2m+1}, so swz(r) >> 1 must
-//    differ among those rows (D = 64: among the 4 rows of one parity) -> 16 distinct
-//    16-byte bank groups.
-// swz depends only on r & 15, so moving by a multiple of 16 rows keeps offsets.
+// chunk c of row r is stored at chunk position c ^ swz(r).  The LDS has 64 banks of 4
+// bytes (256 bytes per bank row), and the swizzle keeps both read patterns of the
+// 16x16x32 operands conflict-free under the way gfx950 serves them (measured with an
+// in-bounds probe: a pair of lanes on one bank costs an extra cycle only inside one
+// service group):
+//  * ds_read_b128 (row reads of MFMA operands) is served in four groups of 16 lanes,
+//    {0-3, 12-15, 20-23, 24-27}, {4-7, 8-11, 16-19, 28-31} and the same two plus 32; each
+//    group must touch 16 distinct 16-byte bank groups.  The kernels' row reads put lane
+//    16 g + c on row c (mod 16) at logical chunk 4 ks + g, so a group holds rows
+//    {0-3, 12-15} of one g and rows {4-11} of g ^ 1: swz maps rows 4..11 onto whole
+//    chunk pairs {2k, 2k+1} (positions 8..15 at D = 128) and rows {0-3, 12-15} onto the
+//    other pairs; the two g of a group differ in bit 0 of the chunk, which maps every
+//    pair onto itself, so the two halves of a group stay apart.  (The earlier swizzle, 2 (r & 7) + (r >> 3 & 1), was conflict-free for groups of
+//    16 consecutive lanes and measured 8.2 instead of 4.7 cycles per read.)
+//  * ds_read_b64_tr_b16 (transposing reads) is served as one 64-lane request in at least
+//    two cycles, one more for each further distinct address on a bank.  Lane 16 g + c reads
+//    row 4 g + c / 4 (mod 16) at logical chunks {2m, 2m + 1}, i.e. physical pair
+//    m ^ (swz(r) >> 1); swz(r) >> 1 takes distinct values on rows 0..7 and on rows 8..15
+//    (at D = 64 on the rows of one parity, which share a 256-byte bank row), so every bank
+//    holds exactly two of the 512 bytes (this also holds if the request were split into
+//    32-lane halves).
+// At D = 64 two rows share one bank row (r & 1 selects its half), and the same
+// construction applies to the rows of each parity.  swz depends only on r & 15, so moving
+// by a multiple of 16 rows keeps offsets.
 //
 // buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at M0 + 16*l, i.e. one
 // instruction fills 1 KiB of LDS contiguously; the swizzle is applied on the
@@ -27,20 +41,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ __forceinline__ int swz(int r) {
   static_assert(D == 64 || D == 128, "head dim");
-  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  const int b = (r >> 3) & 1;
+  const int pair = D == 128 ? ((r & 7) ^ (b << 2)) : (((r >> 1) & 3) ^ (b << 1));
+  return (pair << 1) | b;
 }
 
 // Byte offset of (row r, logical 16-byte chunk c) inside a tile.
 template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) {
+__host__ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * (2 * D) + ((c ^ swz<D>(r)) << 4);
 }
 
 // Byte offset of the 8-byte group holding elements [col, col+4) of row r (col % 4 == 0).
 template <int D>
-__device__ __forceinline__ int tile_off_tr(int r, int col) {
+__host__ __device__ __forceinline__ int tile_off_tr(int r, int col) {
   return tile_off<D>(r, col >> 3) + 2 * (col & 7);
 }
 
