@@ -591,6 +591,16 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) dpt[b][qb] = mfma16(a, doreg[qb][ks], dpt[b][qb]);
       }
+    // one K or V fragment read per two MFMAs, issued AHEAD fragments early (measured on
+    // the 27280-token shard: 2 ahead 0.6-2% faster than the compiler's own order, 1 ahead
+    // 7% slower, 3 to 6 ahead 0.3% slower)
+    constexpr int AHEAD = 2, R = 4 * NKS;
+    ATTN_SCHED(kSchedDSRead, AHEAD);
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      ATTN_SCHED(kSchedMFMA, 2);
+      if (n + AHEAD < R) ATTN_SCHED(kSchedDSRead, 1);
+    }
   };
   auto mask_scores = [&](uint64_t vw, int k0, int h, f32x4 (&st)[2][2]) {
     // value i of block (b, qb) is key k0 + 32h + 16b + 4g + i of query qw + 16 qb + c;
@@ -631,6 +641,15 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
       const bf16x8 a = lds_tr8(kt + 32 * h * RB, troff[db][0], troff[db][1]);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) dqacc[db][qb] = mfma16(a, ds[qb], dqacc[db][qb]);
+    }
+    // fragments of two transposing reads, two MFMAs each, issued AHEAD fragments early
+    // (2 or 3 ahead: 0.7% faster than the compiler's own order; 4: 0.3%)
+    constexpr int AHEAD = 3, F = ND;
+    ATTN_SCHED(kSchedDSRead, 2 * AHEAD);
+#pragma unroll
+    for (int n = 0; n < F; ++n) {
+      ATTN_SCHED(kSchedMFMA, 2);
+      if (n + AHEAD < F) ATTN_SCHED(kSchedDSRead, 2);
     }
   };
   auto compute = [&](const char* kt, const char* vt, int k0, uint64_t vw) {
