@@ -56,6 +56,19 @@ def run_dense(A, t, causal=False):
     return res
 
 
+# Per-head oracle forwards (out, lse) of the grouped-query and causal shards, kept for the
+# sampled-column tests that need every row's out and LSE: the oracle treats each (batch,
+# head) alone, so a head's forward is the same arithmetic wherever it is computed.
+_FWD = {}
+
+
+def oracle_fwd_head(name, t, h, kh=None, causal=False):
+    if (name, h) not in _FWD:
+        q, k, v, _ = head(t, h, kh)
+        _FWD[(name, h)] = oracle.attn_fwd(q, k, v, causal=causal)
+    return _FWD[(name, h)]
+
+
 def head(t, h, kh=None):
     kh = h if kh is None else kh
     return (f64(t.q[:, :, h:h + 1]), f64(t.k[:, :, kh:kh + 1]), f64(t.v[:, :, kh:kh + 1]),
@@ -140,7 +153,7 @@ def test_wan_shard_gqa_rows_full_head(wan_gqa, h):
     w, t, g = wan_gqa
     G = w.H // w.Hk
     q, k, v, do = head(t, h, h // G)
-    out, lse = oracle.attn_fwd(q, k, v)
+    out, lse = oracle_fwd_head(w.name, t, h, h // G)
     _, dq, _, _ = oracle.attn_bwd(q, k, v, out, lse, do, want_dkdv=False)
     sl = slice(h, h + 1)
     assert_parity(f"out[h{h}]", to_f64(g["out"][:, :, sl]), out)
@@ -159,7 +172,10 @@ def test_wan_shard_gqa_sampled_key_columns(wan_gqa, kv_head):
     heads = slice(kv_head * G, (kv_head + 1) * G)
     q, do = f64(t.q[:, :, heads]), f64(t.do[:, :, heads])
     k, v = f64(t.k[:, :, kv_head:kv_head + 1]), f64(t.v[:, :, kv_head:kv_head + 1])
-    out, lse = oracle.attn_fwd_gqa(q, k, v)
+    # the group's forward, head by head (as attn_fwd_gqa computes it)
+    fw = [oracle_fwd_head(w.name, t, h, kv_head) for h in range(heads.start, heads.stop)]
+    out = np.concatenate([o for o, _ in fw], axis=2)
+    lse = np.concatenate([l for _, l in fw], axis=1)
     _, _, dk, dv = oracle.attn_bwd_gqa(q, k[:, cols], v[:, cols], out, lse, do)
     sl = slice(kv_head, kv_head + 1)
     assert_parity(f"dk[kv{kv_head}]", to_f64(g["dk"][:, cols, sl]), dk)
@@ -181,7 +197,7 @@ def test_wan_shard_causal_rows_full_head(wan_causal, h):
     over keys 0..i)."""
     w, t, g = wan_causal
     q, k, v, do = head(t, h)
-    out, lse = oracle.attn_fwd(q, k, v, causal=True)
+    out, lse = oracle_fwd_head(w.name, t, h, causal=True)
     _, dq, _, _ = oracle.attn_bwd(q, k, v, out, lse, do, want_dkdv=False, causal=True)
     sl = slice(h, h + 1)
     assert_parity(f"out[h{h}]", to_f64(g["out"][:, :, sl]), out)
@@ -199,7 +215,7 @@ def test_wan_shard_causal_sampled_key_columns(wan_causal, h):
     cols = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, S - 2, S - 1],
                                      rng.integers(0, S, 16)]))
     q, k, v, do = head(t, h)
-    out, lse = oracle.attn_fwd(q, k, v, causal=True)
+    out, lse = oracle_fwd_head(w.name, t, h, causal=True)
     rdk, rdv = [], []
     for j in cols:
         _, _, dk, dv = oracle.attn_bwd(q[:, j:], k[:, j:j + 1], v[:, j:j + 1], out[:, j:],
