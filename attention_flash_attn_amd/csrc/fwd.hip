@@ -262,8 +262,12 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     x = fmaxf(x, __shfl_xor(x, 16));
     return fmaxf(x, __shfl_xor(x, 32));
   };
-  auto softmax = [&](int k0, uint64_t vw, auto kbc) __attribute__((always_inline)) {
+  // later_c: a compile-time promise that the rows already have a reference (the dense loop
+  // after its first tile), which drops the per-tile check for a first tile.
+  const std::false_type kMayBeFirst{};
+  auto softmax = [&](int k0, uint64_t vw, auto kbc, auto later_c) __attribute__((always_inline)) {
     constexpr int KB = decltype(kbc)::value, NKB = 2 * KB;
+    constexpr bool kLater = decltype(later_c)::value;
     constexpr uint64_t kFull = KB == 2 ? ~0ull : 0xFFFFFFFFull;  // bits of the tile's keys
     if ((vw & kFull) != kFull || (p.causal && k0 + 32 * KB - 1 > qw)) {
       keep_branch();
@@ -285,13 +289,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     // below 2^14.  The first tile of a row (no reference yet) and the rare rejected tile
     // form the tile max from y (over the row's four lanes), move the reference up by it,
     // rescale O and l, and recompute the weights.
-    const bool first = __ballot(m_run[0] == -INFINITY || m_run[1] == -INFINITY) != 0;
+    const bool first = kLater ? false : __ballot(m_run[0] == -INFINITY || m_run[1] == -INFINITY) != 0;
     float muse[2], lt[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      muse[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-      lt[qb] = 0.f;
-    }
+    for (int qb = 0; qb < 2; ++qb) muse[qb] = kLater ? m_run[qb] : (m_run[qb] == -INFINITY ? 0.f : m_run[qb]);
 #pragma unroll
     for (int s = 0; s < KB; ++s)
 #pragma unroll
@@ -304,7 +305,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
             const float y = fmaf(sacc[2 * s + h][qb][i], c2, -muse[qb]);
             sacc[2 * s + h][qb][i] = y;
             x[4 * h + i] = __builtin_amdgcn_exp2f(y);
-            lt[qb] += x[4 * h + i];
+            // the weights are >= +0, so starting the sum from the first one is exact
+            lt[qb] = (s == 0 && h == 0 && i == 0) ? x[0] : lt[qb] + x[4 * h + i];
           }
         pk[s][qb] = pack8(x, 0);
       }
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if (j + 2 < ntiles) kld.issue(kn, kbase, rsk, (j + 2) * BN, nk);
       if (j + 1 < ntiles) vld.issue(vn, vbase, rsk, (j + 1) * BN, nk);
     }
-    if (vw_s != 0) softmax(j * BN, vw_s, kTwoHalves);
+    if (vw_s != 0) softmax(j * BN, vw_s, kTwoHalves, kMayBeFirst);
   };
   // Both groups run the same sequence, group B one phase later (it passes one barrier
   // before its first phase, group A one after its last), so register lifetimes at every
@@ -403,9 +405,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     auto bar = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
     auto word = [&](int j) -> uint64_t __attribute__((always_inline)) { return kv.word(j * BN, 1u); };
     // VALU phase of tile j (kn: the buffer of K(j+2), vn: the buffer of V(j+1))
-    auto vphase = [&](int j, char* __restrict__ kn, char* __restrict__ vn) __attribute__((always_inline)) {
+    // (after tile 0 every row has a finite reference: no mask, and tile 0 holds a valid key)
+    auto vphase = [&](int j, char* __restrict__ kn, char* __restrict__ vn, auto later_c)
+        __attribute__((always_inline)) {
       if (j + lead < ntiles) cld.issue(grp_b ? vn : kn, cbase, rsk, (j + lead) * BN, nk);
-      softmax(j * BN, vw_s, kTwoHalves);
+      softmax(j * BN, vw_s, kTwoHalves, later_c);
     };
     // pair of phases of tile j, 0 < j < ntiles (kt: K(j), vp: V(j-1))
     auto dpair = [&](int j, const char* __restrict__ kt, const char* __restrict__ vp,
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       vw_s = word(j);
       wait_tile_loads();
       bar();
-      vphase(j, kn, vn);
+      vphase(j, kn, vn, std::true_type{});
       bar();
     };
     // K(0) and K(1) by group A, V(0) by group B, before the first phase
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     vw_s = word(0);
     wait_tile_loads();
     bar();
-    vphase(0, dK2, dV1);
+    vphase(0, dK2, dV1, kMayBeFirst);
     bar();
     for (int j = 1; j < ntiles; j += 3) {  // j % 3 == 1, 2, 0
       dpair(j, dK1, dV0, dK0, dV2);
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       }
       if (j < t1 && vw != 0) {
         gemm_s(kt, kb_c);
-        softmax(j * BNS, vw, kb_c);
+        softmax(j * BNS, vw, kb_c, kMayBeFirst);
         gemm_pv(vt, kb_c);
       }
       wait_tile_loads();

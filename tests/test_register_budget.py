@@ -23,12 +23,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # runs all its products on 16x16x32 MFMAs with two keys (dK/dV) or two queries (dQ) per
 # lane at the 256-register ceiling: the dense instances (plain and accumulating) store
 # five registers before their loops and reload two per dQ key tile; the varlen instance
-# fits without spilling.  The dense D = 128 forward stores two registers before its key
-# loops and reloads them after.  Every other kernel must not spill at all.
+# fits without spilling.  Every other kernel must not spill at all.
 MAX_SCRATCH = {
     "attn::bwd_kernel<128, false, false>": 20,
     "attn::bwd_kernel<128, false, true>": 20,
-    "attn::fwd_kernel<128, false>": 12,
 }
 
 
