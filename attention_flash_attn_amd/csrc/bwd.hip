@@ -218,7 +218,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const Slice sl, D
   for (int h = 0; h < 2; ++h) tr0[h] = tile_off_tr<D>(16 * h + 4 * g + (c >> 2), 4 * (c & 3));
   int qoff[NKS], troff[ND][2];
   auto offsets = [&]() {
-    asm volatile("" : "+v"(qoff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
+    // D = 128: not hoisted out of the loop (registers); D = 64 has room to keep them all
+    if constexpr (D == 128) asm volatile("" : "+v"(qoff0), "+v"(tr0[0]), "+v"(tr0[1]));
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qoff[ks] = qoff0 ^ (64 * ks);
 #pragma unroll
@@ -535,7 +536,8 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const Slice sl, DqS
   for (int h = 0; h < 2; ++h) tr0[h] = tile_off_tr<D>(16 * h + 4 * g + (c >> 2), 4 * (c & 3)) + grp * GB;
   int koff[NKS], troff[ND][2];
   auto offsets = [&]() {
-    asm volatile("" : "+v"(koff0), "+v"(tr0[0]), "+v"(tr0[1]));  // not hoisted out of the loop
+    // D = 128: not hoisted out of the loop (registers); D = 64 has room to keep them all
+    if constexpr (D == 128) asm volatile("" : "+v"(koff0), "+v"(tr0[0]), "+v"(tr0[1]));
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) koff[ks] = koff0 ^ (64 * ks);
 #pragma unroll
