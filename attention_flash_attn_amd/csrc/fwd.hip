@@ -349,10 +349,14 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // copies it issued in its previous phase.
   auto gemm_phase = [&](int j, const char* __restrict__ kt, const char* __restrict__ vp)
       __attribute__((always_inline)) {
+    // The group in its MFMA phase takes priority over the other wave of its SIMD (which runs
+    // softmax): measured 0.5-1% faster than equal priorities on the masked and dense loops.
+    __builtin_amdgcn_s_setprio(1);
     if (vw_s != 0) gemm_pv(vp, kTwoHalves);  // vw_s: still the word of tile j-1
     vw_s = tile_word(j, mbytes);
     mbytes = kv.load((j + 1) * BN);  // clamped: unused past the last tile
     if (vw_s != 0) gemm_s(kt, kTwoHalves);
+    __builtin_amdgcn_s_setprio(0);
     if (grp_b) wait_tile_loads();
   };
   // VALU phase of tile j.  Group B first issues the copies of K(j+2) (into the buffer of
@@ -414,7 +418,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     // pair of phases of tile j, 0 < j < ntiles (kt: K(j), vp: V(j-1))
     auto dpair = [&](int j, const char* __restrict__ kt, const char* __restrict__ vp,
                      char* __restrict__ kn, char* __restrict__ vn) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);  // MFMA phase first (as in gemm_phase)
       gemm_pv_s(vp, kt);
+      __builtin_amdgcn_s_setprio(0);
       vw_s = word(j);
       wait_tile_loads();
       bar();
